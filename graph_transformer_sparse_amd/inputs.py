@@ -1,0 +1,339 @@
+"""Seeded synthetic inputs: CSR graphs and dense node features.
+
+This module is shared by the tests, the benchmark and the oracle's callers.
+It holds none of the attention arithmetic: it only draws random graphs and
+random feature matrices and lays them out.
+
+Stand-ins.  The pages measure on ogbn-arxiv/proteins/products and Reddit
+(Scalable and Adaptive Parallel Training of Graph Transformer on Large
+Graphs, Table 2 and Section 5.2).  Those datasets are not available, so
+power-law and R-MAT generators of similar size and skew stand in for them.
+
+Every array comes from ``np.random.default_rng([cfg, stream])`` (PCG64):
+stream 0 draws the graph, 1 Q, 2 K, 3 V, 4 dY and 5 the per-edge bias.
+
+Graph conventions (the adjacency A of the SGA definition, Section 2.1 of
+the paper): row i is the query / destination node, column j the key/value
+source node, A is a 0/1 pattern stored as CSR (int32 indptr and indices),
+the columns of every row strictly ascending, and every row r < n_rows has
+the self-loop (r, r).
+"""
+from __future__ import annotations
+
+import os
+from dataclasses import dataclass, field
+
+import numpy as np
+
+# stream ids of the seeded generators
+S_GRAPH, S_Q, S_K, S_V, S_DY, S_BIAS = 0, 1, 2, 3, 4, 5
+
+
+@dataclass(frozen=True)
+class Config:
+    name: str
+    idx: int           # seed component
+    n_rows: int        # R: query rows (destination nodes)
+    n_cols: int        # M: key/value rows (source nodes)
+    heads: int
+    head_dim: int
+    dtype: str         # "f32" or "bf16"
+    bias: bool
+    desc: str = field(default="", compare=False)
+
+
+CONFIGS = {
+    "tiny": Config("tiny", 0, 2000, 2000, 1, 64, "f32", False,
+                   "Erdos-Renyi directed, mean out-degree 8, self-loops"),
+    "mid": Config("mid", 1, 131072, 131072, 8, 16, "f32", False,
+                  "R-MAT (0.57,0.19,0.19,0.05), 14 draws per node, self-loops"),
+    "large": Config("large", 2, 1 << 20, 1 << 20, 8, 32, "bf16", False,
+                    "Chung-Lu exponent 2.1, mean 16, max weight 50000, self-loops"),
+    "hub": Config("hub", 3, 2_400_000, 2_400_000, 4, 32, "bf16", True,
+                  "Chung-Lu exponent 1.9, 62M nnz, per-edge bias"),
+    "shard": Config("shard", 4, 524288, 4194304, 8, 16, "bf16", False,
+                    "rank-0 row block of a relabelled R-MAT graph on 2^22 nodes"),
+}
+CONFIG_ORDER = ["tiny", "mid", "large", "hub", "shard"]
+
+
+def rng_for(cfg_idx: int, stream: int) -> np.random.Generator:
+    return np.random.default_rng([cfg_idx, stream])
+
+
+# ----------------------------------------------------------------------------
+# CSR assembly
+# ----------------------------------------------------------------------------
+
+def csr_from_pairs(rows, cols, n_rows: int, n_cols: int, self_loops: bool = True):
+    """Deduplicate (row, col) pairs, add self-loops, and return int32 CSR.
+
+    The result has strictly ascending columns within every row.
+    """
+    rows = np.asarray(rows, dtype=np.int64)
+    cols = np.asarray(cols, dtype=np.int64)
+    keys = rows * n_cols + cols
+    if self_loops:
+        loops = np.arange(min(n_rows, n_cols), dtype=np.int64)
+        keys = np.concatenate([keys, loops * n_cols + loops])
+    keys = np.unique(keys)
+    r = keys // n_cols
+    c = keys - r * n_cols
+    counts = np.bincount(r, minlength=n_rows)
+    indptr = np.zeros(n_rows + 1, dtype=np.int64)
+    np.cumsum(counts, out=indptr[1:])
+    assert indptr[-1] < 2**31
+    return indptr.astype(np.int32), c.astype(np.int32)
+
+
+def csr_from_rows(row_lists, n_cols: int):
+    """CSR from explicit per-row column lists (sorted, deduplicated here)."""
+    indptr = [0]
+    idx = []
+    for cols in row_lists:
+        u = sorted(set(int(c) for c in cols))
+        assert all(0 <= c < n_cols for c in u)
+        idx.extend(u)
+        indptr.append(len(idx))
+    return np.asarray(indptr, dtype=np.int32), np.asarray(idx, dtype=np.int32)
+
+
+# ----------------------------------------------------------------------------
+# graph families
+# ----------------------------------------------------------------------------
+
+def gnp_directed(n: int, mean_deg: float, rng) -> tuple:
+    """Directed G(n, p) over ordered pairs i != j with p = mean_deg / (n - 1)."""
+    p = mean_deg / (n - 1)
+    rows, cols = [], []
+    step = max(1, (1 << 22) // n)
+    for r0 in range(0, n, step):
+        r1 = min(n, r0 + step)
+        hit = rng.random((r1 - r0, n)) < p
+        rr, cc = np.nonzero(hit)
+        rr = rr + r0
+        keep = rr != cc
+        rows.append(rr[keep])
+        cols.append(cc[keep])
+    return np.concatenate(rows), np.concatenate(cols)
+
+
+RMAT_ABCD = (0.57, 0.19, 0.19, 0.05)
+
+
+def rmat_pairs(levels: int, n_draws: int, rng, batch: int = 1 << 22):
+    """R-MAT draws: per level one uniform u picks quadrant a/b/c/d for
+    (row bit, col bit), most significant bit first."""
+    a, b, c, _ = RMAT_ABCD
+    t_ab, t_abc = a + b, a + b + c
+    rows = np.empty(n_draws, dtype=np.int64)
+    cols = np.empty(n_draws, dtype=np.int64)
+    for s in range(0, n_draws, batch):
+        m = min(batch, n_draws - s)
+        r = np.zeros(m, dtype=np.int64)
+        cc = np.zeros(m, dtype=np.int64)
+        for _ in range(levels):
+            u = rng.random(m, dtype=np.float32)
+            rb = u >= np.float32(t_ab)                    # quadrants c, d
+            cb = ((u >= np.float32(a)) & ~rb) | (u >= np.float32(t_abc))  # b, d
+            r = (r << 1) | rb
+            cc = (cc << 1) | cb
+        rows[s:s + m] = r
+        cols[s:s + m] = cc
+    return rows, cols
+
+
+def chung_lu_weights(n: int, alpha: float, x_min: float, w_max: float, rng):
+    u = 1.0 - rng.random(n)            # (0, 1]
+    return np.minimum(x_min * u ** (-1.0 / alpha), w_max)
+
+
+def _bisect_xmin(u, alpha, w_max, mean):
+    lo, hi = 1e-3, float(mean)
+    for _ in range(100):
+        mid = 0.5 * (lo + hi)
+        m = np.minimum(mid * u ** (-1.0 / alpha), w_max).mean()
+        if m < mean:
+            lo = mid
+        else:
+            hi = mid
+    return 0.5 * (lo + hi)
+
+
+def _draw_by_weight(cdf, m, rng):
+    return np.searchsorted(cdf, rng.random(m) * cdf[-1], side="right").astype(np.int64)
+
+
+def graph_for(cfg: Config):
+    """(indptr, indices) int32 for one of the named configurations."""
+    rng = rng_for(cfg.idx, S_GRAPH)
+    R, M = cfg.n_rows, cfg.n_cols
+    if cfg.name == "tiny":
+        rows, cols = gnp_directed(R, 8.0, rng)
+        return csr_from_pairs(rows, cols, R, M)
+    if cfg.name == "mid":
+        rows, cols = rmat_pairs(17, 14 * R, rng)
+        return csr_from_pairs(rows, cols, R, M)
+    if cfg.name == "large":
+        u = 1.0 - rng.random(R)
+        xmin = _bisect_xmin(u, 1.1, 50000.0, 16.0)
+        w = np.minimum(xmin * u ** (-1.0 / 1.1), 50000.0)
+        cdf = np.cumsum(w)
+        n = int(round(cdf[-1]))
+        rows = _draw_by_weight(cdf, n, rng)
+        cols = _draw_by_weight(cdf, n, rng)
+        keep = rows != cols
+        return csr_from_pairs(rows[keep], cols[keep], R, M)
+    if cfg.name == "hub":
+        target = 62_000_000
+        w = chung_lu_weights(R, 0.9, 1.0, float(R - 1), rng)
+        cdf = np.cumsum(w)
+        need = target - R
+        kept = np.empty(0, dtype=np.int64)
+        while kept.size < need:
+            m = 20_000_000
+            rows = _draw_by_weight(cdf, m, rng)
+            cols = _draw_by_weight(cdf, m, rng)
+            keys = rows * M + cols
+            keys = keys[rows != cols]
+            # distinct keys of this batch in first-draw order
+            _, first = np.unique(keys, return_index=True)
+            keys = keys[np.sort(first)]
+            if kept.size:
+                srt = np.sort(kept)
+                pos = np.searchsorted(srt, keys)
+                pos[pos == srt.size] = 0
+                keys = keys[srt[pos] != keys]
+            kept = np.concatenate([kept, keys[: need - kept.size]])
+        r = kept // M
+        c = kept - r * M
+        ip, ix = csr_from_pairs(r, c, R, M)
+        assert ix.size == target, ix.size
+        return ip, ix
+    if cfg.name == "shard":
+        n_glob = 1 << 22
+        perm = rng.permutation(n_glob)
+        rows_all, cols_all = [], []
+        n_draws = 32 * n_glob
+        batch = 1 << 23
+        for s in range(0, n_draws, batch):
+            m = min(batch, n_draws - s)
+            r, c = rmat_pairs(22, m, rng)
+            r = perm[r]
+            c = perm[c]
+            keep = r < R
+            rows_all.append(r[keep])
+            cols_all.append(c[keep])
+        return csr_from_pairs(np.concatenate(rows_all), np.concatenate(cols_all), R, M)
+    raise KeyError(cfg.name)
+
+
+# ----------------------------------------------------------------------------
+# features
+# ----------------------------------------------------------------------------
+
+def to_bf16_values(x32: np.ndarray) -> np.ndarray:
+    """Round float32 to bfloat16 (round to nearest even) and return the bf16
+    values widened back to float32, exactly.  NaN/Inf are not produced by the
+    generators, so the plain rounding rule on the bit pattern applies."""
+    u = np.ascontiguousarray(x32, dtype=np.float32).view(np.uint32).astype(np.uint64)
+    u = (u + 0x7FFF + ((u >> 16) & 1)) >> 16
+    return (u.astype(np.uint32) << 16).view(np.float32).reshape(x32.shape)
+
+
+def bf16_bits(x_bf16_values: np.ndarray) -> np.ndarray:
+    """uint16 bit patterns of float32 values that are exact bf16 values."""
+    u = np.ascontiguousarray(x_bf16_values, dtype=np.float32).view(np.uint32)
+    assert not np.any(u & 0xFFFF)
+    return (u >> 16).astype(np.uint16)
+
+
+def features(cfg_idx: int, stream: int, n: int, heads: int, head_dim: int, dtype: str):
+    """[n, heads, head_dim] standard normal features.  Returned as float32
+    holding exactly the values of the requested dtype (bf16 is rounded)."""
+    x = rng_for(cfg_idx, stream).standard_normal((n, heads, head_dim), dtype=np.float32)
+    if dtype == "bf16":
+        x = to_bf16_values(x)
+    return x
+
+
+def edge_bias(cfg_idx: int, nnz: int, heads: int):
+    """[nnz, heads] float32 ~ N(0, variance 0.5), in CSR edge order."""
+    return rng_for(cfg_idx, S_BIAS).normal(0.0, np.sqrt(0.5), (nnz, heads)).astype(np.float32)
+
+
+@dataclass
+class Problem:
+    cfg: Config
+    indptr: np.ndarray
+    indices: np.ndarray
+    Q: np.ndarray
+    K: np.ndarray
+    V: np.ndarray
+    dY: np.ndarray
+    bias: np.ndarray | None
+
+    @property
+    def nnz(self) -> int:
+        return int(self.indices.size)
+
+    @property
+    def scale(self) -> float:
+        return float(self.cfg.head_dim) ** -0.5
+
+
+def _cache_dir():
+    d = os.environ.get("GT_INPUT_CACHE")
+    return d if d else None
+
+
+def make_problem(cfg: Config, graph=None) -> Problem:
+    """All inputs of one configuration.  ``graph`` overrides the graph."""
+    if graph is None:
+        cache = _cache_dir()
+        path = os.path.join(cache, f"graph_{cfg.name}.npz") if cache else None
+        if path and os.path.exists(path):
+            with np.load(path) as z:
+                graph = (z["indptr"], z["indices"])
+        else:
+            graph = graph_for(cfg)
+            if path:
+                os.makedirs(cache, exist_ok=True)
+                tmp = path + ".tmp.npz"
+                np.savez(tmp, indptr=graph[0], indices=graph[1])
+                os.replace(tmp, path)
+    indptr, indices = graph
+    H, dh = cfg.heads, cfg.head_dim
+    Q = features(cfg.idx, S_Q, cfg.n_rows, H, dh, cfg.dtype)
+    K = features(cfg.idx, S_K, cfg.n_cols, H, dh, cfg.dtype)
+    V = features(cfg.idx, S_V, cfg.n_cols, H, dh, cfg.dtype)
+    dY = features(cfg.idx, S_DY, cfg.n_rows, H, dh, cfg.dtype)
+    bias = edge_bias(cfg.idx, int(indices.size), H) if cfg.bias else None
+    return Problem(cfg, indptr, indices, Q, K, V, dY, bias)
+
+
+def small_problem(seed: int, indptr, indices, n_cols: int, heads: int, head_dim: int,
+                  dtype: str = "f32", bias: bool = False, name: str = "small") -> Problem:
+    """Inputs for an explicit small graph (tests)."""
+    R = int(indptr.size - 1)
+    cfg = Config(name, 1000 + seed, R, n_cols, heads, head_dim, dtype, bias)
+    return make_problem(cfg, graph=(np.asarray(indptr, np.int32), np.asarray(indices, np.int32)))
+
+
+def random_graph(seed: int, n_rows: int, n_cols: int, degrees, self_loops: bool = True):
+    """CSR whose row r has exactly degrees[r] distinct columns (including the
+    self-loop when self_loops and r < n_cols).  Columns are uniform without
+    replacement."""
+    rng = np.random.default_rng([2000 + seed, S_GRAPH])
+    rows = []
+    for r in range(n_rows):
+        d = int(degrees[r])
+        assert d <= n_cols
+        if self_loops and r < n_cols and d > 0:
+            others = np.delete(np.arange(n_cols), r)
+            pick = rng.choice(others, size=d - 1, replace=False)
+            cols = np.concatenate([[r], pick])
+        else:
+            cols = rng.choice(n_cols, size=d, replace=False)
+        rows.append(cols)
+    return csr_from_rows(rows, n_cols)
