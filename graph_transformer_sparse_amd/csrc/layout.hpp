@@ -1,0 +1,67 @@
+// Layout of the caller's `meta` buffer of a prepared graph, and the
+// default thresholds of the degree-ordered schedule.
+#pragma once
+#include <stddef.h>
+#include <stdint.h>
+
+#include <algorithm>
+
+namespace gt {
+
+// Segments (rows of A or of A^T) with at most DEFAULT_T_SMALL nonzeros are
+// handled by a lane group inside a wavefront; longer ones by whole
+// wavefronts, in pieces of at most DEFAULT_CHUNK nonzeros.
+constexpr int32_t DEFAULT_T_SMALL = 32;
+constexpr int32_t DEFAULT_CHUNK = 2048;
+
+constexpr int SORT_TILE_ITEMS = 4096;   // items per radix-sort block
+constexpr int SCAN_TILE_ITEMS = 4096;   // items per scan block
+
+// Capacity of a schedule's piece list: sum over big segments of
+// ceil(d / chunk) <= floor(nnz / chunk) + n_seg.
+inline int64_t sched_cap(int64_t n_seg, int64_t nnz, int32_t chunk) {
+  return n_seg + nnz / chunk + 1;
+}
+
+struct MetaLayout {
+  size_t indptr_t, indices_t, perm;
+  size_t row_order, row_items, row_merges;
+  size_t col_order, col_items, col_merges;
+  size_t kA, vA, kB, vB, hist, bsum, misc;
+  size_t total;
+};
+
+inline bool meta_layout(int64_t R, int64_t M, int64_t E, int32_t chunk, MetaLayout *L) {
+  const int64_t LIM = INT32_MAX - 1;
+  if (R < 0 || M < 0 || E < 0 || R > LIM || M > LIM || E > LIM || chunk < 1) return false;
+  size_t off = 0;
+  auto take = [&](int64_t words) {
+    size_t at = off;
+    off += ((size_t)std::max<int64_t>(words, 1) * 4 + 255) / 256 * 256;
+    return at;
+  };
+  const int64_t capR = sched_cap(R, E, chunk), capM = sched_cap(M, E, chunk);
+  L->indptr_t = take(M + 1);
+  L->indices_t = take(E);
+  L->perm = take(E);
+  L->row_order = take(R);
+  L->row_items = take(4 * capR);
+  L->row_merges = take(3 * capR);
+  L->col_order = take(M);
+  L->col_items = take(4 * capM);
+  L->col_merges = take(3 * capM);
+  const int64_t nmax = std::max<int64_t>({E, R, M, 1});
+  const int64_t nblk = (nmax + SORT_TILE_ITEMS - 1) / SORT_TILE_ITEMS;
+  const int64_t scan_len = std::max<int64_t>({256 * nblk, M + 1, R + 1});
+  L->kA = take(nmax);
+  L->vA = take(nmax);
+  L->kB = take(nmax);
+  L->vB = take(nmax);
+  L->hist = take(256 * nblk);
+  L->bsum = take((scan_len + SCAN_TILE_ITEMS - 1) / SCAN_TILE_ITEMS + 1);
+  L->misc = take(64);
+  L->total = off;
+  return true;
+}
+
+}  // namespace gt

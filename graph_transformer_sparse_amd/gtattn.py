@@ -1,0 +1,295 @@
+"""Python binding of libgtattn (include/gt_attn.h), through ctypes.
+
+Argument marshalling only: tensors are allocated with torch on the current
+device, their pointers and the current HIP stream go to the C ABI, and every
+step of the computation runs in the library's kernels.  If the library has
+not been built, every entry point raises; there is no fallback.
+
+Names follow the C ABI: gt_graph_prepare, gt_attn_fwd, gt_attn_bwd,
+gt_attn_work_bytes, gt_csr_validate, gt_default_thresholds, plus the
+autograd wrapper GTAttnFn / sparse_graph_attention.
+"""
+from __future__ import annotations
+
+import ctypes as C
+import os
+import re
+
+import torch
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "_build", "libgtattn.so")
+HEADER = os.path.join(os.path.dirname(HERE), "include", "gt_attn.h")
+
+GT_OK = 0
+GT_F32, GT_BF16 = 0, 1
+GT_VALIDATE_WORK_BYTES = 64
+STATUS = {0: "GT_OK", 1: "GT_E_NULL", 2: "GT_E_ARG", 3: "GT_E_DTYPE", 4: "GT_E_SHAPE",
+          5: "GT_E_ALIGN", 6: "GT_E_UNSUPPORTED", 7: "GT_E_WORKSPACE", 8: "GT_E_CSR",
+          9: "GT_E_HIP"}
+
+_i64, _i32, _P, _f32, _sz = C.c_int64, C.c_int32, C.c_void_p, C.c_float, C.c_size_t
+
+
+class GtSched(C.Structure):
+    _fields_ = [("order", _P), ("items", _P), ("merges", _P),
+                ("n_seg", _i64), ("n_big", _i64), ("n_mid", _i64), ("n_small", _i64),
+                ("n_items", _i64), ("n_merges", _i64), ("max_degree", _i64)]
+
+
+class GtGraph(C.Structure):
+    _fields_ = [("n_rows", _i64), ("n_cols", _i64), ("nnz", _i64),
+                ("indptr", _P), ("indices", _P),
+                ("indptr_t", _P), ("indices_t", _P), ("perm", _P),
+                ("rows", GtSched), ("cols", GtSched),
+                ("t_small", _i32), ("t_mid", _i32), ("chunk", _i32), ("reserved", _i32)]
+
+
+class GTError(RuntimeError):
+    def __init__(self, status: int, where: str, detail: str):
+        super().__init__(f"{where}: {STATUS.get(status, status)} ({detail})")
+        self.status = status
+
+
+_lib = None
+
+
+def header_functions() -> list[str]:
+    """Names of the functions include/gt_attn.h declares."""
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(gt_[a-z0-9_]+)\s*\(", text)))
+
+
+def lib():
+    """The loaded library; raises if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"{LIB_PATH} is missing: build it with graph_transformer_sparse_amd.build")
+    L = C.CDLL(LIB_PATH)
+    G = C.POINTER(GtGraph)
+    sig = {
+        "gt_graph_meta_bytes": (_sz, [_i64, _i64, _i64, _i32]),
+        "gt_graph_prepare": (_i32, [_P, _P, _i64, _i64, _i64, _i32, _i32, _i32, _P, _sz, G, _P]),
+        "gt_default_thresholds": (None, [C.POINTER(_i32)] * 3),
+        "gt_csr_validate": (_i32, [_P, _P, _i64, _i64, _i64, _P, _sz, C.POINTER(_i32), _P]),
+        "gt_attn_work_bytes": (_sz, [G, _i32, _i32]),
+        "gt_attn_fwd": (_i32, [G, _i32, _i32, _i32, _f32, _P, _P, _P, _P, _P, _P, _P, _sz, _P]),
+        "gt_attn_bwd": (_i32, [G, _i32, _i32, _i32, _f32, _P, _P, _P, _P, _P, _P,
+                               _P, _P, _P, _P, _P, _sz, _P]),
+        "gt_prof_enable": (_i32, [_i32]),
+        "gt_prof_reset": (_i32, []),
+        "gt_prof_query": (_i32, [C.c_char_p, C.POINTER(C.c_double), C.POINTER(_i64)]),
+        "gt_status_str": (C.c_char_p, [_i32]),
+        "gt_last_error": (C.c_char_p, []),
+        "gt_version": (_i32, []),
+    }
+    for name, (res, args) in sig.items():
+        f = getattr(L, name)
+        f.restype = res
+        f.argtypes = args
+    _lib = L
+    return L
+
+
+def _check(status: int, where: str):
+    if status != GT_OK:
+        raise GTError(status, where, lib().gt_last_error().decode())
+
+
+def _ptr(t):
+    return None if t is None else C.c_void_p(t.data_ptr())
+
+
+def _stream(device=None):
+    return C.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _dt(dtype) -> int:
+    if dtype == torch.float32:
+        return GT_F32
+    if dtype == torch.bfloat16:
+        return GT_BF16
+    raise TypeError(f"unsupported dtype {dtype}")
+
+
+def gt_default_thresholds():
+    a, b, c = _i32(), _i32(), _i32()
+    lib().gt_default_thresholds(C.byref(a), C.byref(b), C.byref(c))
+    return a.value, b.value, c.value
+
+
+class Graph:
+    """A CSR adjacency prepared for attention (transpose and schedules).
+
+    Holds the device CSR, the meta buffer and the filled gt_graph struct."""
+
+    def __init__(self, st: GtGraph, meta: torch.Tensor, indptr: torch.Tensor,
+                 indices: torch.Tensor):
+        self.st = st
+        self.meta = meta
+        self.indptr = indptr
+        self.indices = indices
+
+    @property
+    def n_rows(self):
+        return self.st.n_rows
+
+    @property
+    def n_cols(self):
+        return self.st.n_cols
+
+    @property
+    def nnz(self):
+        return self.st.nnz
+
+    def _view(self, ptr: int, n: int) -> torch.Tensor:
+        base = self.meta.data_ptr()
+        off = ptr - base
+        assert off % 4 == 0 and 0 <= off and off + 4 * n <= self.meta.numel()
+        return self.meta.view(torch.int32)[off // 4: off // 4 + n]
+
+    @property
+    def indptr_t(self):
+        return self._view(self.st.indptr_t, self.n_cols + 1)
+
+    @property
+    def indices_t(self):
+        return self._view(self.st.indices_t, self.nnz)
+
+    @property
+    def perm(self):
+        return self._view(self.st.perm, self.nnz)
+
+    def schedule(self, which: str) -> dict:
+        s = self.st.rows if which == "rows" else self.st.cols
+        return dict(order=self._view(s.order, s.n_seg),
+                    counts=(s.n_big, s.n_mid, s.n_small),
+                    items=self._view(s.items, 4 * s.n_items).view(-1, 4),
+                    merges=self._view(s.merges, 3 * s.n_merges).view(-1, 3),
+                    max_degree=s.max_degree)
+
+
+def gt_graph_prepare(indptr: torch.Tensor, indices: torch.Tensor, n_cols: int,
+                     t_small: int | None = None, t_mid: int | None = None,
+                     chunk: int | None = None) -> Graph:
+    """Prepare a device CSR (int32 indptr/indices) for attention."""
+    L = lib()
+    d_small, d_mid, d_chunk = gt_default_thresholds()
+    t_small = d_small if t_small is None else t_small
+    t_mid = d_mid if t_mid is None else t_mid
+    chunk = d_chunk if chunk is None else chunk
+    assert indptr.dtype == torch.int32 and indices.dtype == torch.int32
+    assert indptr.is_contiguous() and indices.is_contiguous()
+    R, E = indptr.numel() - 1, indices.numel()
+    nb = L.gt_graph_meta_bytes(R, n_cols, E, chunk)
+    if nb == 0:
+        raise GTError(2, "gt_graph_meta_bytes", "sizes out of range")
+    meta = torch.empty(nb, dtype=torch.uint8, device=indptr.device)
+    st = GtGraph()
+    _check(L.gt_graph_prepare(_ptr(indptr), _ptr(indices) if E else None, R, n_cols, E,
+                              t_small, t_mid, chunk, _ptr(meta), nb, C.byref(st),
+                              _stream(indptr.device)), "gt_graph_prepare")
+    return Graph(st, meta, indptr, indices)
+
+
+def gt_csr_validate(indptr: torch.Tensor, indices: torch.Tensor, n_cols: int) -> int:
+    """The CSR check code (0 valid, 1-4 as gt_attn.h)."""
+    work = torch.empty(GT_VALIDATE_WORK_BYTES, dtype=torch.uint8, device=indptr.device)
+    code = _i32(-1)
+    st = lib().gt_csr_validate(_ptr(indptr), _ptr(indices) if indices.numel() else None,
+                               indptr.numel() - 1, n_cols, indices.numel(), _ptr(work),
+                               GT_VALIDATE_WORK_BYTES, C.byref(code), _stream(indptr.device))
+    if st not in (GT_OK, 8):
+        _check(st, "gt_csr_validate")
+    return code.value
+
+
+def gt_attn_work_bytes(g: Graph, heads: int, head_dim: int) -> int:
+    return int(lib().gt_attn_work_bytes(C.byref(g.st), heads, head_dim))
+
+
+def _work(g, heads, head_dim, device, work):
+    nb = gt_attn_work_bytes(g, heads, head_dim)
+    if work is None or work.numel() < nb:
+        work = torch.empty(nb, dtype=torch.uint8, device=device)
+    return work
+
+
+def gt_attn_fwd(g: Graph, Q, K, V, bias=None, scale=None, work=None, Y=None, lse=None):
+    """Forward: returns (Y, lse).  Q [R,H,dh], K/V [M,H,dh] (f32 or bf16)."""
+    R, H, dh = Q.shape
+    scale = dh ** -0.5 if scale is None else float(scale)
+    for t in (Q, K, V):
+        assert t.is_contiguous() and t.dtype == Q.dtype
+    if bias is not None:
+        assert bias.dtype == torch.float32 and bias.is_contiguous()
+    Y = torch.empty_like(Q) if Y is None else Y
+    lse = torch.empty((R, H), dtype=torch.float32, device=Q.device) if lse is None else lse
+    work = _work(g, H, dh, Q.device, work)
+    _check(lib().gt_attn_fwd(C.byref(g.st), H, dh, _dt(Q.dtype), scale, _ptr(Q), _ptr(K),
+                             _ptr(V), _ptr(bias), _ptr(Y), _ptr(lse), _ptr(work),
+                             work.numel(), _stream(Q.device)), "gt_attn_fwd")
+    return Y, lse
+
+
+def gt_attn_bwd(g: Graph, Q, K, V, lse, dY, bias=None, scale=None, work=None,
+                dQ=None, dK=None, dV=None, dbias=None):
+    """Backward: returns (dQ, dK, dV, dbias); dbias is None without bias."""
+    R, H, dh = Q.shape
+    scale = dh ** -0.5 if scale is None else float(scale)
+    for t in (Q, K, V, dY):
+        assert t.is_contiguous() and t.dtype == Q.dtype
+    dQ = torch.empty_like(Q) if dQ is None else dQ
+    dK = torch.empty_like(K) if dK is None else dK
+    dV = torch.empty_like(V) if dV is None else dV
+    if bias is not None and dbias is None:
+        dbias = torch.empty_like(bias)
+    work = _work(g, H, dh, Q.device, work)
+    _check(lib().gt_attn_bwd(C.byref(g.st), H, dh, _dt(Q.dtype), scale, _ptr(Q), _ptr(K),
+                             _ptr(V), _ptr(bias), _ptr(lse), _ptr(dY), _ptr(dQ),
+                             _ptr(dK), _ptr(dV), _ptr(dbias), _ptr(work), work.numel(),
+                             _stream(Q.device)), "gt_attn_bwd")
+    return dQ, dK, dV, dbias
+
+
+def prof_enable(on: bool = True):
+    _check(lib().gt_prof_enable(1 if on else 0), "gt_prof_enable")
+
+
+def prof_reset():
+    _check(lib().gt_prof_reset(), "gt_prof_reset")
+
+
+def prof_query(kernel: str):
+    """(total milliseconds, launches) recorded for a kernel since the reset."""
+    ms, n = C.c_double(), _i64()
+    _check(lib().gt_prof_query(kernel.encode(), C.byref(ms), C.byref(n)), "gt_prof_query")
+    return ms.value, n.value
+
+
+class GTAttnFn(torch.autograd.Function):
+    """Sparse graph attention as an autograd function over a prepared graph."""
+
+    @staticmethod
+    def forward(ctx, g: Graph, Q, K, V, bias=None, scale=None):
+        Q, K, V = Q.contiguous(), K.contiguous(), V.contiguous()
+        bias = None if bias is None else bias.contiguous()
+        Y, lse = gt_attn_fwd(g, Q, K, V, bias, scale)
+        ctx.g, ctx.scale = g, scale
+        ctx.save_for_backward(Q, K, V, lse, bias if bias is not None else torch.empty(0))
+        ctx.has_bias = bias is not None
+        return Y
+
+    @staticmethod
+    def backward(ctx, dY):
+        Q, K, V, lse, bias = ctx.saved_tensors
+        bias = bias if ctx.has_bias else None
+        dQ, dK, dV, db = gt_attn_bwd(ctx.g, Q, K, V, lse, dY.contiguous(), bias, ctx.scale)
+        return None, dQ, dK, dV, db, None
+
+
+def sparse_graph_attention(g: Graph, Q, K, V, bias=None, scale=None):
+    return GTAttnFn.apply(g, Q, K, V, bias, scale)

@@ -1,0 +1,206 @@
+/*
+ * gt_attn.h -- C ABI of the MI355X (gfx950) sparse graph attention library
+ * (libgtattn.so).
+ *
+ * The operation is multi-head sparse graph attention over a CSR adjacency,
+ * as defined in "Scalable and Adaptive Parallel Training of Graph
+ * Transformer on Large Graphs" (Section 2.1, Eq. 1-5; backward operator
+ * structure in Section 2.2):
+ *
+ *   for every stored edge e = (i, j) of A and every head h
+ *     s_e,h   = scale * <Q[i,h,:], K[j,h,:]> + bias[e,h]       (SDDMM)
+ *     U_e,h   = exp(s_e,h) / sum_{e' in row i} exp(s_e',h)     (softmax over
+ *               the stored neighbours j in N(i) of row i only, Eq. 1-2)
+ *     Y[i,h,:] = sum_{e in row i} U_e,h V[j,h,:]                (SpMM, Eq. 5)
+ *     lse[i,h] = log sum_{e in row i} exp(s_e,h)
+ *   backward (the gradients of the same expression):
+ *     dU_e,h = <dY[i,h,:], V[j,h,:]>                            (sampled SDDMM)
+ *     dS_e,h = U_e,h (dU_e,h - sum_{e' in row i} U_e',h dU_e',h)
+ *     dQ[i,h,:] = scale * sum_{e in row i}    dS_e,h K[j,h,:]   (SpMM)
+ *     dK[j,h,:] = scale * sum_{e in column j} dS_e,h Q[i,h,:]   (SpMM, A^T)
+ *     dV[j,h,:] =         sum_{e in column j} U_e,h dY[i,h,:]   (SpMM, A^T)
+ *     dbias[e,h] = dS_e,h
+ *
+ * Readings of the method: row i is the query (destination) node and column j
+ * the key/value (source) node; head h owns channels [h*dh, (h+1)*dh) of a
+ * node's contiguous H*dh feature row (the [n, h, d'] layout of the paper's
+ * Algorithm 1); the scale is passed in (1/sqrt(dh) in the paper's use); the
+ * optional per-edge bias is added, unscaled, to the score before the softmax
+ * (the MegaGraph page, Section III-A1, mechanism 3).  An empty row gives
+ * Y = 0, lse = -inf and dQ = 0; an empty column gives dK = dV = 0.
+ *
+ * Conventions shared by every entry point
+ *   - Every array argument is DEVICE memory, owned by the caller.  The
+ *     library never allocates, frees or keeps device memory between calls;
+ *     scratch comes in through the `meta` / `work` arguments, sized by the
+ *     *_bytes query functions.
+ *   - `stream` is a hipStream_t (NULL = the default stream).  Calls enqueue
+ *     work on it and return, except gt_graph_prepare and gt_csr_validate,
+ *     which synchronise that stream before returning (both run once per
+ *     graph).
+ *   - Dense features are row-major [n, heads, head_dim] (node-major, heads
+ *     contiguous), in the dtype `dt`; rows start 16-byte aligned.
+ *     Supported: head_dim in {16, 32, 64}, heads in {1, 2, 4, 8}, and
+ *     heads * head_dim * sizeof(dt) <= 1024 bytes (a row fits one wavefront
+ *     at 16 bytes a lane).  Softmax statistics (lse),
+ *     bias and dbias are float32.  All arithmetic is float32; bf16 inputs
+ *     are widened exactly and bf16 outputs are rounded to nearest even.
+ *   - CSR: indptr[n_rows + 1], indices[nnz], int32, columns strictly
+ *     ascending within a row, 0 <= column < n_cols.  The content is trusted
+ *     (gt_csr_validate checks it); n_rows, n_cols, nnz < 2^31 - 1.
+ *   - Results are bitwise deterministic: no floating-point atomics, fixed
+ *     summation orders, and the CSR transpose is stable.
+ *   - Errors are reported only through the gt_status return value (with a
+ *     per-thread detail string from gt_last_error); a call that fails its
+ *     argument checks launches nothing and touches no device memory.
+ */
+#ifndef GT_ATTN_H
+#define GT_ATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef int32_t gt_status;
+enum {
+  GT_OK = 0,
+  GT_E_NULL = 1,        /* a required pointer is NULL */
+  GT_E_ARG = 2,         /* a size / count / threshold is out of range */
+  GT_E_DTYPE = 3,       /* unknown dtype */
+  GT_E_SHAPE = 4,       /* heads / head_dim combination not supported */
+  GT_E_ALIGN = 5,       /* a feature array is not 16-byte aligned */
+  GT_E_UNSUPPORTED = 6, /* bias and dbias not given together */
+  GT_E_WORKSPACE = 7,   /* meta / work buffer smaller than required */
+  GT_E_CSR = 8,         /* gt_csr_validate found a malformed CSR */
+  GT_E_HIP = 9          /* the HIP runtime reported an error */
+};
+
+typedef enum { GT_F32 = 0, GT_BF16 = 1 } gt_dtype;
+
+/* Degree-ordered work schedule of the segments (rows of the CSR, or rows
+ * of its transpose = columns of A).  Definition:
+ *   order    = segment ids sorted by degree descending, ties by ascending id;
+ *   n_big    = #segments with degree >  t_mid   (they lead `order`);
+ *   n_mid    = #segments with t_small < degree <= t_mid (next in `order`);
+ *   n_small  = #segments with degree <= t_small (the tail of `order`);
+ *   items    = [n_items][4] int32: every big segment s, in `order`, with
+ *              degree d is cut into nch = ceil(d / chunk) pieces; piece c is
+ *              (s, ptr[s] + floor(c d / nch), ptr[s] + floor((c+1) d / nch),
+ *              slot) where slot is the item's own index if nch > 1, else -1;
+ *   merges   = [n_merges][3] int32: (s, first item, nch) for every big
+ *              segment with nch > 1.
+ * Big pieces and mid segments are each processed by one 64-lane wavefront;
+ * small segments by a group of lanes inside a wavefront.  Split segments
+ * are reduced afterwards in piece order, so results are deterministic. */
+typedef struct gt_sched {
+  int32_t *order;   /* [n_seg] */
+  int32_t *items;   /* [cap][4] */
+  int32_t *merges;  /* [cap][3] */
+  int64_t n_seg, n_big, n_mid, n_small, n_items, n_merges, max_degree;
+} gt_sched;
+
+/* A prepared graph.  Filled by gt_graph_prepare; the device arrays it points
+ * to live in the caller's `meta` buffer (and the caller's indptr/indices),
+ * so the struct is valid as long as those buffers are. */
+typedef struct gt_graph {
+  int64_t n_rows, n_cols, nnz;
+  const int32_t *indptr, *indices;   /* the caller's CSR, [n_rows+1], [nnz] */
+  int32_t *indptr_t;                 /* [n_cols+1] CSR^T row pointer */
+  int32_t *indices_t;                /* [nnz] source row of transposed entry t */
+  int32_t *perm;                     /* [nnz] CSR edge id of transposed entry t */
+  gt_sched rows, cols;               /* schedules over rows of A and of A^T */
+  int32_t t_small, t_mid, chunk;     /* thresholds the schedules were built with */
+  int32_t reserved;
+} gt_graph;
+
+/* ---- graph preparation (once per graph) ------------------------------- */
+
+/* Bytes of device memory gt_graph_prepare needs in `meta` for this graph
+ * size and chunk (persistent arrays plus sort scratch).  0 on bad sizes. */
+size_t gt_graph_meta_bytes(int64_t n_rows, int64_t n_cols, int64_t nnz, int32_t chunk);
+
+/* Build the CSR transpose and both work schedules on the GPU.
+ *   CSR^T: indptr_t[c+1] - indptr_t[c] = in-degree of column c; the entries
+ *   of a column are ordered by ascending source row (a stable transpose);
+ *   indices_t[t] = source row, perm[t] = CSR edge id (the adjacency's
+ *   transpose is what the backward's A^T products of Section 2.2 run on).
+ *   Thresholds: 0 <= t_small <= t_mid, chunk >= 1 (gt_default_thresholds).
+ * Synchronises `stream` (the schedule sizes are read back to fill *out).
+ * Errors: GT_E_NULL, GT_E_ARG, GT_E_WORKSPACE (meta_bytes too small),
+ * GT_E_HIP. */
+gt_status gt_graph_prepare(const int32_t *indptr, const int32_t *indices, int64_t n_rows,
+                           int64_t n_cols, int64_t nnz, int32_t t_small, int32_t t_mid,
+                           int32_t chunk, void *meta, size_t meta_bytes, gt_graph *out,
+                           void *stream);
+
+/* The thresholds the kernels are tuned for: t_small, t_mid, chunk. */
+void gt_default_thresholds(int32_t *t_small, int32_t *t_mid, int32_t *chunk);
+
+/* Debug check of CSR content (the oracle's codes): 0 valid; 1 indptr[0] != 0
+ * or indptr[n_rows] != nnz; 2 indptr decreasing; 3 a column outside
+ * [0, n_cols); 4 columns of a row not strictly ascending.  When several
+ * apply, the first in that order wins, and among 3/4 the lowest edge id.
+ * `work` is GT_VALIDATE_WORK_BYTES of device scratch.  Writes the code to
+ * *code; returns GT_E_CSR if it is not 0.  Synchronises `stream`.
+ * Errors: GT_E_NULL, GT_E_ARG, GT_E_WORKSPACE, GT_E_CSR, GT_E_HIP. */
+#define GT_VALIDATE_WORK_BYTES 64
+gt_status gt_csr_validate(const int32_t *indptr, const int32_t *indices, int64_t n_rows,
+                          int64_t n_cols, int64_t nnz, void *work, size_t work_bytes,
+                          int32_t *code, void *stream);
+
+/* ---- attention -------------------------------------------------------- */
+
+/* Bytes of `work` gt_attn_fwd / gt_attn_bwd need (the larger of the two):
+ * partial softmax states of split rows, the backward's per-row statistics
+ * (lse, D) and partial gradient sums of split rows and columns. */
+size_t gt_attn_work_bytes(const gt_graph *g, int32_t heads, int32_t head_dim);
+
+/* Forward (Eq. 4-5): Y [n_rows, heads, head_dim] in dt, lse [n_rows, heads]
+ * float32.  Q is [n_rows, heads, head_dim], K and V [n_cols, heads,
+ * head_dim], all dt.  bias (nullable) is [nnz, heads] float32 in CSR edge
+ * order.  Z and U are never materialised: the kernel makes one pass over
+ * each row's edges with an online (running max) softmax.
+ * Errors: GT_E_NULL, GT_E_DTYPE, GT_E_SHAPE, GT_E_ALIGN, GT_E_WORKSPACE,
+ * GT_E_HIP. */
+gt_status gt_attn_fwd(const gt_graph *g, int32_t heads, int32_t head_dim, gt_dtype dt,
+                      float scale, const void *Q, const void *K, const void *V,
+                      const float *bias, void *Y, float *lse, void *work, size_t work_bytes,
+                      void *stream);
+
+/* Backward (Section 2.2): given lse of gt_attn_fwd and the output gradient
+ * dY [n_rows, heads, head_dim], writes dQ [n_rows, heads, head_dim], dK, dV
+ * [n_cols, heads, head_dim] (all dt, every element written) and, iff bias is
+ * given, dbias [nnz, heads] float32 (bias and dbias must both be NULL or both
+ * non-NULL; else GT_E_UNSUPPORTED).  The softmax weights are recomputed from
+ * lse.  A pass over the rows of A computes the row term
+ * D_i = sum_e U_e dU_e and dQ; a pass over the rows of A^T computes dK, dV
+ * and dbias.  No output element is written by more than one wavefront and
+ * nothing uses atomics.
+ * Errors: as gt_attn_fwd, plus GT_E_UNSUPPORTED. */
+gt_status gt_attn_bwd(const gt_graph *g, int32_t heads, int32_t head_dim, gt_dtype dt,
+                      float scale, const void *Q, const void *K, const void *V,
+                      const float *bias, const float *lse, const void *dY, void *dQ, void *dK,
+                      void *dV, float *dbias, void *work, size_t work_bytes, void *stream);
+
+/* ---- instrumentation and misc ----------------------------------------- */
+
+/* When enabled, every kernel launch is bracketed by HIP events on its own
+ * stream, and gt_prof_query returns the summed device time and the launch
+ * count per kernel name ("fwd", "fwd_merge", "bwd_rows", "bwd_rows_merge",
+ * "bwd_cols", "bwd_cols_merge").  gt_prof_query synchronises the events. */
+gt_status gt_prof_enable(int32_t on);
+gt_status gt_prof_reset(void);
+gt_status gt_prof_query(const char *kernel, double *total_ms, int64_t *launches);
+
+const char *gt_status_str(gt_status s);
+/* Detail of the last failed call on this thread ("" if none). */
+const char *gt_last_error(void);
+int32_t gt_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* GT_ATTN_H */

@@ -1,0 +1,65 @@
+"""Helpers of the GPU tests: device copies of seeded problems and the
+parity comparison.
+
+Tolerance (fp32 1e-5, bf16 inputs with fp32 accumulation 2e-2, both
+relative): per tensor and head, |got - ref| <= rtol*|ref| + rtol*rms(ref)
+elementwise, where rms is over the head's compared elements; lse compares as
+|got - ref| <= rtol*max(1, |ref|), and -inf (empty rows) must match exactly.
+"""
+import numpy as np
+import torch
+
+RTOL = {"f32": 1e-5, "bf16": 2e-2}
+TDT = {"f32": torch.float32, "bf16": torch.bfloat16}
+
+
+def dev(x, dtype=None, device="cuda"):
+    if x is None:
+        return None
+    t = torch.from_numpy(np.ascontiguousarray(x))
+    if dtype is not None:
+        t = t.to(dtype)
+    return t.to(device).contiguous()
+
+
+def to_np(t):
+    return t.detach().float().cpu().numpy().astype(np.float64)
+
+
+def assert_close(got, ref, rtol, name):
+    g = got if isinstance(got, np.ndarray) else to_np(got)
+    ref = np.asarray(ref, np.float64)
+    assert g.shape == ref.shape, (name, g.shape, ref.shape)
+    if ref.size == 0:
+        return
+    axes = tuple(a for a in range(ref.ndim) if a != 1) if ref.ndim >= 2 else (0,)
+    rms = np.sqrt(np.mean(ref ** 2, axis=axes, keepdims=True))
+    bound = rtol * np.abs(ref) + rtol * rms
+    err = np.abs(g - ref)
+    bad = ~(err <= bound)
+    if bad.any():
+        idx = np.unravel_index(np.argmax(np.where(bad, err / np.maximum(bound, 1e-300), 0)), ref.shape)
+        rel = np.linalg.norm(g - ref) / max(np.linalg.norm(ref), 1e-300)
+        raise AssertionError(f"{name}: {int(bad.sum())} of {bad.size} outside tolerance; "
+                             f"worst at {idx}: got {g[idx]!r} ref {ref[idx]!r} bound {bound[idx]!r}; "
+                             f"rel l2 {rel:.3e}")
+
+
+def assert_lse(got, ref, rtol, name="lse"):
+    g = got if isinstance(got, np.ndarray) else to_np(got)
+    ref = np.asarray(ref, np.float64)
+    ninf = np.isneginf(ref)
+    assert np.array_equal(np.isneginf(g), ninf), f"{name}: -inf pattern differs"
+    f = ~ninf
+    err = np.abs(g[f] - ref[f])
+    bound = rtol * np.maximum(1.0, np.abs(ref[f]))
+    assert np.all(err <= bound), f"{name}: max err {err.max()} vs bound {bound[np.argmax(err)]}"
+
+
+def device_problem(P, device="cuda"):
+    """Device tensors of a Problem: (indptr, indices, Q, K, V, dY, bias)."""
+    dt = TDT[P.cfg.dtype]
+    return dict(indptr=dev(P.indptr, device=device), indices=dev(P.indices, device=device),
+                Q=dev(P.Q, dt, device), K=dev(P.K, dt, device), V=dev(P.V, dt, device),
+                dY=dev(P.dY, dt, device),
+                bias=dev(P.bias, torch.float32, device) if P.bias is not None else None)

@@ -1,0 +1,139 @@
+"""The C ABI library without a GPU: it loads, exports every function the
+header declares, and its host-side argument checks return the documented
+status codes before anything touches the device (fake device pointers are
+never dereferenced on these paths)."""
+import ctypes as C
+import os
+
+import pytest
+
+from graph_transformer_sparse_amd import build as B
+from graph_transformer_sparse_amd import gtattn as T
+
+
+def _fresh():
+    srcs = [os.path.join(B.CSRC, f) for f in os.listdir(B.CSRC)]
+    srcs.append(os.path.join(B.INCLUDE, "gt_attn.h"))
+    return os.path.exists(B.LIB) and os.path.getmtime(B.LIB) >= max(map(os.path.getmtime, srcs))
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not _fresh():
+        B.build()
+    return T.lib()
+
+
+def test_exports_every_declared_function(L):
+    names = T.header_functions()
+    assert "gt_attn_fwd" in names and "gt_attn_bwd" in names and "gt_graph_prepare" in names
+    for n in names:
+        assert hasattr(L, n), n
+    assert L.gt_version() >= 100
+
+
+def test_status_strings(L):
+    for code in range(10):
+        assert L.gt_status_str(code)
+    assert L.gt_status_str(99) == b"unknown status"
+
+
+def test_default_thresholds(L):
+    ts, tm, ch = T.gt_default_thresholds()
+    assert 0 <= ts <= tm and ch >= 1
+
+
+def _fake_graph(R=100, M=80, E=500, n_items=3):
+    g = T.GtGraph()
+    g.n_rows, g.n_cols, g.nnz = R, M, E
+    fake = 0x10000000
+    g.indptr, g.indices, g.indptr_t, g.indices_t, g.perm = fake, fake, fake, fake, fake
+    for s in (g.rows, g.cols):
+        s.order, s.items, s.merges = fake, fake, fake
+        s.n_items = n_items
+    return g
+
+
+FAKE = C.c_void_p(0x20000000)      # 16-byte aligned, never dereferenced here
+ODD = C.c_void_p(0x20000004)
+
+
+def _fwd(L, g, heads=4, dh=32, dt=T.GT_F32, Q=FAKE, K=FAKE, V=FAKE, bias=None, Y=FAKE,
+         lse=FAKE, work=FAKE, nb=1 << 30):
+    return L.gt_attn_fwd(C.byref(g) if g is not None else None, heads, dh, dt, 0.1, Q, K, V,
+                         bias, Y, lse, work, nb, None)
+
+
+def test_fwd_argument_checks(L):
+    g = _fake_graph()
+    assert _fwd(L, None) == 1                       # NULL graph
+    assert _fwd(L, g, dt=7) == 3                    # dtype
+    assert _fwd(L, g, dh=48) == 4                   # head_dim
+    assert _fwd(L, g, heads=3) == 4                 # heads
+    assert _fwd(L, g, heads=8, dh=64) == 4          # 2 KiB rows in fp32
+    assert _fwd(L, g, Q=None) == 1
+    assert _fwd(L, g, K=ODD) == 5
+    assert _fwd(L, g, lse=None) == 1
+    assert _fwd(L, g, work=None) == 1
+    assert _fwd(L, g, nb=16) == 7                   # workspace too small
+    assert b"work has 16 bytes" in L.gt_last_error()
+    ung = _fake_graph()
+    ung.rows.order = None
+    assert _fwd(L, ung) == 1                        # not prepared
+
+
+def test_bwd_argument_checks(L):
+    g = _fake_graph()
+
+    def bwd(bias=None, dbias=None, dQ=FAKE, nb=1 << 30, heads=4):
+        return L.gt_attn_bwd(C.byref(g), heads, 32, T.GT_BF16, 0.1, FAKE, FAKE, FAKE, bias,
+                             FAKE, FAKE, dQ, FAKE, FAKE, dbias, FAKE, nb, None)
+
+    assert bwd(bias=FAKE) == 6                      # bias without dbias
+    assert bwd(dbias=FAKE) == 6
+    assert bwd(dQ=ODD) == 5
+    assert bwd(nb=64) == 7
+    assert bwd(heads=16) == 4
+
+
+def test_work_bytes_grow_with_graph(L):
+    g = _fake_graph(n_items=0)
+    a = L.gt_attn_work_bytes(C.byref(g), 4, 32)
+    g2 = _fake_graph(n_items=100)
+    b = L.gt_attn_work_bytes(C.byref(g2), 4, 32)
+    assert b > a > 0
+    # backward: per-row statistics (lse, D) = 8 bytes per row and head
+    assert a >= 100 * 4 * 8
+
+
+def test_prepare_argument_checks(L):
+    mb = L.gt_graph_meta_bytes(100, 80, 500, 64)
+    assert mb > 4 * (2 * 500 + 81)
+    assert L.gt_graph_meta_bytes(-1, 80, 500, 64) == 0
+    assert L.gt_graph_meta_bytes(100, 80, 500, 0) == 0
+    assert L.gt_graph_meta_bytes(1 << 31, 80, 500, 64) == 0
+    out = T.GtGraph()
+
+    def prep(indptr=FAKE, indices=FAKE, ts=4, tm=8, ch=8, meta=FAKE, nb=mb, o=True):
+        return L.gt_graph_prepare(indptr, indices, 100, 80, 500, ts, tm, ch, meta, nb,
+                                  C.byref(out) if o else None, None)
+
+    assert prep(o=False) == 1
+    assert prep(indptr=None) == 1
+    assert prep(meta=None) == 1
+    assert prep(ts=9) == 2                           # t_small > t_mid
+    assert prep(ch=0) == 2
+    assert prep(nb=mb - 1) == 7
+
+
+def test_validate_argument_checks(L):
+    code = C.c_int32(-1)
+    assert L.gt_csr_validate(None, FAKE, 10, 10, 5, FAKE, 64, C.byref(code), None) == 1
+    assert L.gt_csr_validate(FAKE, FAKE, 10, 10, 5, FAKE, 8, C.byref(code), None) == 7
+    assert L.gt_csr_validate(FAKE, FAKE, -1, 10, 5, FAKE, 64, C.byref(code), None) == 2
+
+
+def test_prof_query_checks(L):
+    ms, n = C.c_double(), C.c_int64()
+    assert L.gt_prof_query(b"nope", C.byref(ms), C.byref(n)) == 2
+    assert L.gt_prof_query(b"fwd", C.byref(ms), C.byref(n)) == 0 and n.value == 0

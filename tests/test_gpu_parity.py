@@ -1,0 +1,122 @@
+"""Parity of the HIP path with the fp64 oracle: forward (Y, lse) and backward
+(dQ, dK, dV, dbias), through the C ABI, on seeded inputs.
+
+* a sweep of small graphs whose degrees sit on and around the schedule's
+  thresholds (empty rows, rows of 1, 2, 63, 64, 65 nonzeros, split rows and
+  columns with ragged last pieces), rectangular adjacencies, every supported
+  head count / head size / dtype, with and without bias;
+* the 2,000-node config in full, under several thresholds;
+* bitwise determinism.
+The large configurations are in test_gpu_configs.py.
+"""
+import numpy as np
+import pytest
+import torch
+
+from graph_transformer_sparse_amd import gtattn as T
+from graph_transformer_sparse_amd import inputs as I
+from oracle import oracle as O
+
+from gpu_util import RTOL, assert_close, assert_lse, device_problem
+
+pytestmark = pytest.mark.gpu
+
+
+def run_gpu(P, th=None):
+    d = device_problem(P)
+    g = T.gt_graph_prepare(d["indptr"], d["indices"], P.cfg.n_cols, *(th or ()))
+    Y, lse = T.gt_attn_fwd(g, d["Q"], d["K"], d["V"], d["bias"], P.scale)
+    dQ, dK, dV, dB = T.gt_attn_bwd(g, d["Q"], d["K"], d["V"], lse, d["dY"], d["bias"], P.scale)
+    torch.cuda.synchronize()
+    return Y, lse, dQ, dK, dV, dB
+
+
+def check_full(P, out, rtol=None):
+    rtol = RTOL[P.cfg.dtype] if rtol is None else rtol
+    Y, lse, dQ, dK, dV, dB = out
+    M = P.cfg.n_cols
+    rY, rl = O.fwd(P.indptr, P.indices, M, P.Q, P.K, P.V, P.bias, P.scale)
+    rQ, rK, rV, rB = O.bwd(P.indptr, P.indices, M, P.Q, P.K, P.V, P.dY, P.bias, P.scale)
+    assert_close(Y, rY, rtol, "Y")
+    assert_lse(lse, rl, 1e-5 if P.cfg.dtype == "f32" else 1e-4)
+    assert_close(dQ, rQ, rtol, "dQ")
+    assert_close(dK, rK, rtol, "dK")
+    assert_close(dV, rV, rtol, "dV")
+    if P.bias is not None:
+        assert_close(dB, rB, rtol, "dbias")
+    else:
+        assert dB is None
+
+
+def _degrees(rng, R, M):
+    base = [0, 1, 2, 3, 7, 8, 9, 31, 32, 33, 63, 64, 65, 127, 128, 129, 200]
+    d = np.array([min(x, M) for x in base] + list(rng.integers(0, min(M, 70), R - len(base))))
+    rng.shuffle(d)
+    return d
+
+
+SHAPES = [  # dtype, heads, head_dim
+    ("f32", 1, 64), ("f32", 8, 16), ("f32", 2, 32), ("f32", 4, 64), ("f32", 8, 32),
+    ("bf16", 8, 32), ("bf16", 4, 32), ("bf16", 8, 16), ("bf16", 1, 16), ("bf16", 8, 64),
+    ("bf16", 2, 64), ("f32", 1, 16),
+]
+THRESH = [None, (2, 8, 8), (4, 16, 5), (0, 0, 3)]
+
+
+@pytest.mark.parametrize("shape", SHAPES, ids=[f"{a}-h{b}-d{c}" for a, b, c in SHAPES])
+@pytest.mark.parametrize("bias", [False, True], ids=["nobias", "bias"])
+def test_small_graphs(shape, bias):
+    dt, H, dh = shape
+    k = SHAPES.index(shape) * 2 + int(bias)
+    rng = np.random.default_rng(k)
+    R, M = (120, 260) if k % 3 == 0 else ((260, 90) if k % 3 == 1 else (220, 220))
+    degs = _degrees(rng, R, M)
+    ip, ix = I.random_graph(300 + k, R, M, degs, self_loops=False)
+    P = I.small_problem(k, ip, ix, M, H, dh, dt, bias)
+    for th in THRESH:
+        print(f"small {shape} bias={bias} th={th}", flush=True)
+        check_full(P, run_gpu(P, th))
+
+
+def test_tiny_config():
+    P = I.make_problem(I.CONFIGS["tiny"])
+    for th in (None, (2, 6, 4), (16, 16, 7)):
+        print(f"tiny th={th}", flush=True)
+        check_full(P, run_gpu(P, th))
+
+
+def test_scale_other_than_default():
+    ip, ix = I.random_graph(9, 64, 64, np.full(64, 12))
+    P = I.small_problem(9, ip, ix, 64, 4, 16, "f32", True)
+    d = device_problem(P)
+    g = T.gt_graph_prepare(d["indptr"], d["indices"], 64, 2, 8, 8)
+    Y, lse = T.gt_attn_fwd(g, d["Q"], d["K"], d["V"], d["bias"], 0.3)
+    dQ, dK, dV, dB = T.gt_attn_bwd(g, d["Q"], d["K"], d["V"], lse, d["dY"], d["bias"], 0.3)
+    rY, rl = O.fwd(ip, ix, 64, P.Q, P.K, P.V, P.bias, 0.3)
+    rQ, rK, rV, rB = O.bwd(ip, ix, 64, P.Q, P.K, P.V, P.dY, P.bias, 0.3)
+    for a, b, n in ((Y, rY, "Y"), (dQ, rQ, "dQ"), (dK, rK, "dK"), (dV, rV, "dV"), (dB, rB, "dB")):
+        assert_close(a, b, 1e-5, n)
+    assert_lse(lse, rl, 1e-5)
+
+
+def test_bitwise_determinism():
+    P = I.make_problem(I.CONFIGS["tiny"])
+    a = run_gpu(P, (2, 6, 4))
+    b = run_gpu(P, (2, 6, 4))
+    for x, y in zip(a, b):
+        if x is not None:
+            assert torch.equal(x, y)
+
+
+def test_autograd_function_matches_abi():
+    ip, ix = I.random_graph(11, 80, 80, np.random.default_rng(1).integers(1, 40, 80))
+    P = I.small_problem(11, ip, ix, 80, 4, 32, "bf16", True)
+    d = device_problem(P)
+    g = T.gt_graph_prepare(d["indptr"], d["indices"], 80, 2, 8, 8)
+    q, k, v, b = (d[n].clone().requires_grad_() for n in ("Q", "K", "V", "bias"))
+    y = T.sparse_graph_attention(g, q, k, v, b)
+    y.backward(d["dY"])
+    ref = run_gpu(P, (2, 8, 8))
+    assert torch.equal(y.detach(), ref[0])
+    assert torch.equal(q.grad, ref[2]) and torch.equal(k.grad, ref[3])
+    assert torch.equal(v.grad, ref[4]) and torch.equal(b.grad, ref[5])
