@@ -1,0 +1,236 @@
+"""Benchmark: fused sparse graph attention forward + backward on one MI355X.
+
+One step = gt_attn_fwd + gt_attn_bwd over one synthetic graph and feature
+set (every kernel of the hot path: the fused forward, the backward row pass,
+the backward column pass over the transpose, and the merges of split rows and
+columns).  The graph is prepared once, outside the timed region (its time is
+reported separately); inputs, outputs and workspaces are resident in HBM and
+allocated before timing.
+
+Prints ONE JSON line (rank 0) with the throughput in GEdges/s (edges =
+stored nonzeros, self-loops included) and, for the dominant kernel, the
+achieved fraction of the HBM roofline from the byte model below, timed with
+HIP events inside the library on the stream the kernels run on.  Beside it,
+the fp64 CPU oracle is timed on this host's cores on a bounded sample of the
+same workload.
+
+Byte model (algorithmic bytes: what each kernel must move between HBM and
+the ALUs; s = bytes per element, D = H*dh, b = 1 with a per-edge bias):
+  fwd       R (4 + 2Ds + 4H)                     + E (4 + 2Ds + 4Hb)
+  bwd_rows  R (4 + 3Ds + 12H)                    + E (4 + 2Ds + 4Hb)
+  bwd_cols  M (4 + 2Ds) + M_nz 2Ds               + E (4 + 2Ds + 8H + (4 + 8H)b)
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import re
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+KERNELS = ["fwd", "fwd_merge", "bwd_rows", "bwd_rows_merge", "bwd_cols", "bwd_cols_merge"]
+CSRC = os.path.join(ROOT, "graph_transformer_sparse_amd", "csrc")
+
+
+def byte_model(cfg, R, M, E, M_nz):
+    s = 4 if cfg.dtype == "f32" else 2
+    H, D = cfg.heads, cfg.heads * cfg.head_dim
+    b = 1 if cfg.bias else 0
+    return {
+        "fwd": R * (4 + 2 * D * s + 4 * H) + E * (4 + 2 * D * s + 4 * H * b),
+        "bwd_rows": R * (4 + 3 * D * s + 12 * H) + E * (4 + 2 * D * s + 4 * H * b),
+        "bwd_cols": M * (4 + 2 * D * s) + M_nz * 2 * D * s
+        + E * (4 + 2 * D * s + 8 * H + (4 + 8 * H) * b),
+    }
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for f in sorted(os.listdir(CSRC)):
+        with open(os.path.join(CSRC, f), "rb") as fh:
+            h.update(f.encode() + b"\0" + fh.read())
+    return h.hexdigest()[:16]
+
+
+def traffic_record(kernel: str, workload: str):
+    """HBM bytes per launch from the committed rocprofv3 counter summary of
+    this kernel and workload, if it was taken on the current kernel sources."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{kernel}_{workload}.txt")
+    if not os.path.exists(path):
+        return None
+    rec = {}
+    for line in open(path):
+        m = re.match(r"^([a-z_]+):\s*(\S+)", line.strip())
+        if m:
+            rec[m.group(1)] = m.group(2)
+    if rec.get("source_hash") != kernel_source_hash():
+        return None
+    try:
+        return float(rec["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def cpu_baseline(P, budget_s: float):
+    """The oracle (fp64, OpenMP) on a row block of the same workload whose
+    size is picked so the run takes about budget_s seconds."""
+    from oracle import oracle as O
+    cfg = P.cfg
+    # calibrate on a small row block, then size the measured block
+    def block(k):
+        ip = P.indptr[: k + 1]
+        e = int(ip[-1])
+        return ip, P.indices[:e], (P.bias[:e] if P.bias is not None else None), e
+
+    def run(k):
+        ip, ix, bias, e = block(k)
+        t = time.perf_counter()
+        O.fwd(ip, ix, cfg.n_cols, P.Q[:k], P.K, P.V, bias, P.scale)
+        O.bwd(ip, ix, cfg.n_cols, P.Q[:k], P.K, P.V, P.dY[:k], bias, P.scale)
+        return time.perf_counter() - t, e
+
+    R = cfg.n_rows
+    k = min(R, 4096)
+    t, e = run(k)
+    while t < 0.5 and k < R:
+        k = min(R, k * 4)
+        t, e = run(k)
+    if k < R and t < budget_s:
+        k = min(R, int(k * budget_s / max(t, 1e-3)))
+        t, e = run(k)
+    runs, total = 1, t
+    while total < budget_s:      # the whole workload is cheaper than the budget: repeat it
+        t, e = run(k)
+        runs += 1
+        total += t
+    return {"value": e * runs / total / 1e9, "unit": "GEdges/s", "cores": O.threads(),
+            "kind": "oracle",
+            "sample": (f"rows 0..{k - 1} of the {cfg.name} workload ({e} of {P.nnz} edges, "
+                       f"all {cfg.n_cols} key/value rows), fwd+bwd in float64, {runs} run(s) "
+                       f"in {total:.1f} s")}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--config", default="mid",
+                    choices=["tiny", "mid", "large", "hub", "shard"])
+    ap.add_argument("--cpu-budget", type=float, default=15.0,
+                    help="seconds of oracle work for the CPU baseline (0: skip)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported "
+              "(the multi-GPU sharding is described, not built)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    from graph_transformer_sparse_amd import gtattn as T
+    from graph_transformer_sparse_amd import inputs as I
+
+    T.lib()
+    cfg = I.CONFIGS[args.config]
+    t0 = time.perf_counter()
+    P = I.make_problem(cfg)
+    gen_s = time.perf_counter() - t0
+    dev = torch.device("cuda:0")
+    tdt = torch.float32 if cfg.dtype == "f32" else torch.bfloat16
+    put = lambda x, dt: torch.from_numpy(np.ascontiguousarray(x)).to(dt).to(dev).contiguous()
+    indptr, indices = put(P.indptr, torch.int32), put(P.indices, torch.int32)
+    Q, K, V, dY = (put(x, tdt) for x in (P.Q, P.K, P.V, P.dY))
+    bias = put(P.bias, torch.float32) if P.bias is not None else None
+    R, M, E, H, dh = cfg.n_rows, cfg.n_cols, P.nnz, cfg.heads, cfg.head_dim
+
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    g = T.gt_graph_prepare(indptr, indices, M)
+    torch.cuda.synchronize()
+    prep_ms = (time.perf_counter() - t0) * 1e3
+
+    Y = torch.empty_like(Q)
+    lse = torch.empty((R, H), dtype=torch.float32, device=dev)
+    dQ, dK, dV = torch.empty_like(Q), torch.empty_like(K), torch.empty_like(V)
+    dbias = torch.empty_like(bias) if bias is not None else None
+    work = torch.empty(T.gt_attn_work_bytes(g, H, dh), dtype=torch.uint8, device=dev)
+
+    def step():
+        T.gt_attn_fwd(g, Q, K, V, bias, P.scale, work, Y, lse)
+        T.gt_attn_bwd(g, Q, K, V, lse, dY, bias, P.scale, work, dQ, dK, dV, dbias)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    T.prof_reset()
+    T.prof_enable(True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    T.prof_enable(False)
+    ms_step = elapsed * 1e3 / args.steps
+
+    kern = {}
+    for k in KERNELS:
+        tot, n = T.prof_query(k)
+        if n:
+            kern[k] = {"ms_per_launch": tot / n, "launches": n}
+    M_nz = int(np.count_nonzero(np.diff(T_np(g.indptr_t))))
+    model = byte_model(cfg, R, M, E, M_nz)
+    dominant = max((k for k in model if k in kern), key=lambda k: kern[k]["ms_per_launch"])
+    for k in model:
+        if k in kern:
+            kern[k]["model_GB"] = model[k] / 1e9
+            kern[k]["GBps"] = model[k] / (kern[k]["ms_per_launch"] * 1e-3) / 1e9
+    ach = kern[dominant]["GBps"]
+    traffic = traffic_record(dominant, cfg.name)
+    total_model = sum(model.values())
+
+    line = {
+        "metric": "GEdges/s fused sparse-attn fwd+bwd, 1 MI355X; achieved HBM GB/s vs peak",
+        "value": E / (ms_step * 1e-3) / 1e9,
+        "unit": "GEdges/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic (seeded generators standing in for the pages' graphs)",
+        "config": {"workload": f"{cfg.name}: {cfg.desc}", "nodes": R, "kv_nodes": M, "nnz": E,
+                   "heads": H, "head_dim": dh, "storage": cfg.dtype, "bias": cfg.bias,
+                   "parallelism": "single GPU"},
+        "roofline": {"bound": "hbm", "kernel": dominant, "achieved": ach, "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": ach / HBM_PEAK_GBS,
+                     "traffic": traffic},
+        "cpu_baseline": None,
+        "detail": {"step_model_GB": total_model / 1e9,
+                   "step_GBps": total_model / (ms_step * 1e-3) / 1e9,
+                   "step_frac": total_model / (ms_step * 1e-3) / 1e9 / HBM_PEAK_GBS,
+                   "kernels": kern, "prep_ms": prep_ms, "input_gen_s": gen_s,
+                   "kernel_source_hash": kernel_source_hash()},
+    }
+    if args.cpu_budget > 0:
+        line["cpu_baseline"] = cpu_baseline(P, args.cpu_budget)
+    print(json.dumps(line), flush=True)
+
+
+def T_np(t):
+    return t.cpu().numpy()
+
+
+if __name__ == "__main__":
+    main()

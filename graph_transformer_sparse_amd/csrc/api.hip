@@ -105,7 +105,7 @@ WorkLayout work_layout(const gt_graph *g, int heads, int head_dim) {
   w.fwd_total = w.part_acc + align256(sr * D * sizeof(float));
   w.rowstat = 0;
   w.part_rows = align256((size_t)g->n_rows * heads * 2 * sizeof(float));
-  w.part_cols = w.part_rows + align256(sr * (2 * D + heads) * sizeof(float));
+  w.part_cols = w.part_rows + align256(sr * (2 * D + 3 * heads) * sizeof(float));
   w.bwd_total = w.part_cols + align256(sc * 2 * D * sizeof(float));
   w.total = std::max<size_t>(std::max(w.fwd_total, w.bwd_total), 256);
   return w;

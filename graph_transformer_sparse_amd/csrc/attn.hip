@@ -261,10 +261,18 @@ __global__ __launch_bounds__(BLOCK) void k_fwd_merge(FwdArgs a) {
 // ---------------------------------------------------------------------------
 // backward, row pass over A: dQ and the per-row (lse2, D) statistics
 //
-// With p_e = U_e and dU_e = <dY_i, V_j>, the row term is D_i = sum_e p_e dU_e
-// and dQ_i = scale sum_e p_e (dU_e - D_i) K_j = scale (A1 - D_i A2) with
-// A1 = sum_e p_e dU_e K_j and A2 = sum_e p_e K_j, so one pass over the row's
-// edges gives D, A1 and A2 together.
+// With U_e = p_e / L, p_e = 2^(s2_e - lse2_i) recomputed from the forward's
+// log-sum-exp and L = sum_e p_e (1 up to the rounding of lse), and
+// dU_e = <dY_i, V_j>, the row term is D_i = sum_e U_e dU_e and
+// dQ_i = scale sum_e U_e (dU_e - D_i) K_j.  One pass over the row's edges
+// accumulates, around a shift c (the dU of the first edge a lane group sees),
+//   L = sum p,  S = sum p (dU - c),  A1 = sum p (dU - c) K,  A2 = sum p K,
+// and then D = c + S / L and dQ = scale (A1 - (S / L) A2) / L.  Dividing by L
+// makes the weights sum to 1 whatever the rounding of lse (the column pass
+// gets lse2 + log2(L) so that its weights are the same U_e); the shift keeps
+// the subtraction small, and a row with one edge gets dQ = 0 and D = dU
+// exactly.  Two partial states combine at the shift of the first non-empty
+// one: S = S_a + S_b + (c_b - c_a) L_b, A1 = A1_a + A1_b + (c_b - c_a) A2_b.
 // ---------------------------------------------------------------------------
 struct BwdArgs {
   Sched rows, cols;
@@ -275,11 +283,50 @@ struct BwdArgs {
   const float *lse, *bias;
   void *dQ, *dK, *dV;
   float *dbias;
-  float2 *rowstat;        // [R][H] (lse * log2(e), D)
-  float *part_rows;       // [slots][2D + H]: A1, A2, D of split-row pieces
+  float2 *rowstat;        // [R][H] (lse * log2(e) + log2(L), D)
+  float *part_rows;       // [slots][2D + 3H]: A1, A2, S, L, c of split-row pieces
   float *part_cols;       // [slots][2D]: dK partial, then dV partial
   float qscale, scale;
 };
+
+// Row-pass state of one lane: its N channels of A1 and A2, and the per-head
+// L, S and shift c (equal on the HL lanes of a head).
+template <int N> struct RowState {
+  float a1[N], a2[N], s, l, c;
+};
+
+// st (+)= o, at the shift of st unless st is empty.
+template <int N> __device__ inline void row_merge(RowState<N> &st, const RowState<N> &o) {
+  if (st.l == 0.f) {
+    st = o;
+    return;
+  }
+  const float dc = o.c - st.c;
+  st.s += o.s + dc * o.l;
+  st.l += o.l;
+#pragma unroll
+  for (int c = 0; c < N; ++c) {
+    st.a1[c] += o.a1[c] + dc * o.a2[c];
+    st.a2[c] += o.a2[c];
+  }
+}
+
+// dQ and the row statistics of one row from its state (all lanes of the
+// row's group; lane gl holds channels [gl*N, gl*N + N)).
+template <typename T, int HL, int H>
+__device__ inline void finish_row(const BwdArgs &a, int64_t row, int gl, int h, float lse2,
+                                  const RowState<Vec<T>::N> &st) {
+  constexpr int N = Vec<T>::N, D = HL * H * N;
+  const float inv = st.l > 0.f ? 1.f / st.l : 0.f;
+  const float ds = st.s * inv;
+  float g[N];
+#pragma unroll
+  for (int c = 0; c < N; ++c) g[c] = a.scale * ((st.a1[c] - ds * st.a2[c]) * inv);
+  Vec<T>::store((T *)a.dQ + row * D + gl * N, g);
+  if (gl % HL == 0)
+    a.rowstat[row * H + h] =
+        st.l > 0.f ? make_float2(lse2 + fast_log2(st.l), st.c + ds) : make_float2(-INFINITY, 0.f);
+}
 
 template <typename T, int HL, int H, int U, bool BIAS>
 __global__ __launch_bounds__(BLOCK) void k_bwd_rows(BwdArgs a) {
@@ -295,10 +342,12 @@ __global__ __launch_bounds__(BLOCK) void k_bwd_rows(BwdArgs a) {
 #pragma unroll
   for (int c = 0; c < N; ++c) q[c] *= a.qscale;
   const float lse2 = a.lse[row * H + h] * LOG2E;
-  float a1[N], a2[N], dsum = 0.f;
+  RowState<N> st;
+  st.s = st.l = st.c = 0.f;
 #pragma unroll
-  for (int c = 0; c < N; ++c) a1[c] = a2[c] = 0.f;
+  for (int c = 0; c < N; ++c) st.a1[c] = st.a2[c] = 0.f;
   const int gstart = wk.wave_item ? grp : 0, gstep = wk.wave_item ? RPW : 1;
+  bool first = true;
   for (int64_t e = (int64_t)wk.eb + gstart; e < wk.ee; e += (int64_t)gstep * U) {
     int32_t j[U];
     bool ok[U];
@@ -335,47 +384,54 @@ __global__ __launch_bounds__(BLOCK) void k_bwd_rows(BwdArgs a) {
       s = group_sum<HL>(s);
       du = group_sum<HL>(du);
       if constexpr (BIAS) s += b[u];
+      if (u == 0 && first) st.c = du;   // edge e is valid in every round
       const float p = ok[u] ? fast_exp2(s - lse2) : 0.f;
-      const float pdu = p * du;
-      dsum += pdu;
+      const float pt = p * (du - st.c);
+      st.l += p;
+      st.s += pt;
 #pragma unroll
       for (int c = 0; c < N; ++c) {
-        a1[c] = fmaf(pdu, kx[c], a1[c]);
-        a2[c] = fmaf(p, kx[c], a2[c]);
+        st.a1[c] = fmaf(pt, kx[c], st.a1[c]);
+        st.a2[c] = fmaf(p, kx[c], st.a2[c]);
       }
     }
+    first = false;
   }
   if (wk.wave_item) {
 #pragma unroll
     for (int off = G; off < WAVE; off <<= 1) {
-      dsum += __shfl_xor(dsum, off);
+      RowState<N> o;
+      o.s = __shfl_xor(st.s, off);
+      o.l = __shfl_xor(st.l, off);
+      o.c = __shfl_xor(st.c, off);
 #pragma unroll
       for (int c = 0; c < N; ++c) {
-        a1[c] += __shfl_xor(a1[c], off);
-        a2[c] += __shfl_xor(a2[c], off);
+        o.a1[c] = __shfl_xor(st.a1[c], off);
+        o.a2[c] = __shfl_xor(st.a2[c], off);
       }
+      row_merge(st, o);
     }
     if (grp != 0) return;
     if (wk.slot >= 0) {
-      float *pa = a.part_rows + (int64_t)wk.slot * (2 * D + H);
+      float *pa = a.part_rows + (int64_t)wk.slot * (2 * D + 3 * H);
 #pragma unroll
       for (int c = 0; c < N; ++c) {
-        pa[gl * N + c] = a1[c];
-        pa[D + gl * N + c] = a2[c];
+        pa[gl * N + c] = st.a1[c];
+        pa[D + gl * N + c] = st.a2[c];
       }
-      if (gl % HL == 0) pa[2 * D + h] = dsum;
+      if (gl % HL == 0) {
+        pa[2 * D + h] = st.s;
+        pa[2 * D + H + h] = st.l;
+        pa[2 * D + 2 * H + h] = st.c;
+      }
       return;
     }
   }
-  float g[N];
-#pragma unroll
-  for (int c = 0; c < N; ++c) g[c] = a.scale * (a1[c] - dsum * a2[c]);
-  Vec<T>::store((T *)a.dQ + row * D + gl * N, g);
-  if (gl % HL == 0) a.rowstat[row * H + h] = make_float2(lse2, dsum);
+  finish_row<T, HL, H>(a, row, gl, h, lse2, st);
 }
 
-// Split rows: sum the pieces' (A1, A2, D) in piece order, then dQ and the
-// row statistics.
+// Split rows: combine the pieces' states in piece order, then dQ and the row
+// statistics.
 template <typename T, int HL, int H>
 __global__ __launch_bounds__(BLOCK) void k_bwd_rows_merge(BwdArgs a) {
   constexpr int N = Vec<T>::N, G = HL * H, D = G * N;
@@ -385,23 +441,24 @@ __global__ __launch_bounds__(BLOCK) void k_bwd_rows_merge(BwdArgs a) {
   const int gl = lane, h = gl / HL;
   const int32_t *rec = a.rows.merges + 3 * w;
   const int64_t row = rec[0], first = rec[1], nch = rec[2];
-  float a1[N], a2[N], dsum = 0.f;
+  RowState<N> st;
+  st.s = st.l = st.c = 0.f;
 #pragma unroll
-  for (int c = 0; c < N; ++c) a1[c] = a2[c] = 0.f;
+  for (int c = 0; c < N; ++c) st.a1[c] = st.a2[c] = 0.f;
   for (int64_t k = 0; k < nch; ++k) {
-    const float *pa = a.part_rows + (first + k) * (2 * D + H);
+    const float *pa = a.part_rows + (first + k) * (2 * D + 3 * H);
+    RowState<N> o;
 #pragma unroll
     for (int c = 0; c < N; ++c) {
-      a1[c] += pa[gl * N + c];
-      a2[c] += pa[D + gl * N + c];
+      o.a1[c] = pa[gl * N + c];
+      o.a2[c] = pa[D + gl * N + c];
     }
-    dsum += pa[2 * D + h];
+    o.s = pa[2 * D + h];
+    o.l = pa[2 * D + H + h];
+    o.c = pa[2 * D + 2 * H + h];
+    row_merge(st, o);
   }
-  float g[N];
-#pragma unroll
-  for (int c = 0; c < N; ++c) g[c] = a.scale * (a1[c] - dsum * a2[c]);
-  Vec<T>::store((T *)a.dQ + row * D + gl * N, g);
-  if (gl % HL == 0) a.rowstat[row * H + h] = make_float2(a.lse[row * H + h] * LOG2E, dsum);
+  finish_row<T, HL, H>(a, row, gl, h, a.lse[row * H + h] * LOG2E, st);
 }
 
 // ---------------------------------------------------------------------------
@@ -415,11 +472,9 @@ __global__ __launch_bounds__(BLOCK) void k_bwd_cols(BwdArgs a) {
   if (!wk.active) return;
   const T *Qp = (const T *)a.Q, *dYp = (const T *)a.dY;
   const int64_t col = wk.seg;
-  float kq[N], v[N];
-  Vec<T>::load((const T *)a.K + col * D + gl * N, kq);
+  float k[N], v[N];
+  Vec<T>::load((const T *)a.K + col * D + gl * N, k);
   Vec<T>::load((const T *)a.V + col * D + gl * N, v);
-#pragma unroll
-  for (int c = 0; c < N; ++c) kq[c] *= a.qscale;
   float ak[N], av[N];
 #pragma unroll
   for (int c = 0; c < N; ++c) ak[c] = av[c] = 0.f;
@@ -456,11 +511,12 @@ __global__ __launch_bounds__(BLOCK) void k_bwd_cols(BwdArgs a) {
       float qx[N], gx[N];
       unpack(qr[u], qx);
       unpack(gr[u], gx);
+      // same operands and order as the row pass, so s, p and dU match it
       float s = 0.f, du = 0.f;
 #pragma unroll
       for (int c = 0; c < N; ++c) {
-        s = fmaf(kq[c], qx[c], s);
-        du = fmaf(v[c], gx[c], du);
+        s = fmaf(qx[c] * a.qscale, k[c], s);
+        du = fmaf(gx[c], v[c], du);
       }
       s = group_sum<HL>(s);
       du = group_sum<HL>(du);

@@ -178,17 +178,27 @@ static double score(const prob_t *p, i64 i, i64 e, int h) {
   return s;
 }
 
+/* Outputs of one row pass; every pointer may be NULL.
+ * Y[D], lse[H], dQ[D], Dsum[H] (sum_e U_e dU_e), dB (deg*H, CSR edge order of
+ * the row), and the magnitudes of the sums that define Y and dQ:
+ *   Ymag[h,c]  = sum_e U_e |V[j,h,c]|
+ *   dQmag[h,c] = scale sum_e U_e (|dU_e| + |D|) |K[j,h,c]|
+ * (the sum of the absolute values of the terms, with the term dS_e =
+ * U_e (dU_e - D) bounded by U_e (|dU_e| + |D|)); Tm (deg*H) gets
+ * U_e (|dU_e| + |D|) for the column side. */
+typedef struct {
+  double *Y, *lse, *dQ, *Dsum, *dB, *Ymag, *dQmag, *Tm;
+} row_out_t;
+
 /* Everything the definition gives for one row i, all heads.
- * U, dU, dS: scratch of deg*H doubles ([edge-in-row][head]).
- * Outputs (each may be NULL): Y[D], lse[H], dQ[D], D_out[H] (row sums
- * sum_e U_e dU_e), dB (deg*H, in CSR edge order of the row).
- * The backward part runs only when dQ, dB or D_out is requested. */
-static void row_pass(const prob_t *p, i64 i, double *U, double *dU, double *dS, double *Y,
-                     double *lse, double *dQ, double *D_out, double *dB) {
+ * U, dU, dS: scratch of deg*H doubles ([edge-in-row][head]); U and dS hold
+ * the row's softmax weights and score gradients on return.
+ * The backward part runs only when a backward output is requested. */
+static void row_pass(const prob_t *p, i64 i, double *U, double *dU, double *dS,
+                     const row_out_t *o) {
   const i64 e0 = p->indptr[i], deg = p->indptr[i + 1] - e0;
   const int H = p->H, dh = p->dh;
-  const i64 D = (i64)H * dh;
-  const int want_bwd = (dQ || dB || D_out);
+  const int want_bwd = (o->dQ || o->dB || o->Dsum || o->dQmag || o->Tm);
   for (int h = 0; h < H; ++h) {
     /* scores and softmax over the stored neighbours of row i */
     double m = -INFINITY;
@@ -200,38 +210,44 @@ static void row_pass(const prob_t *p, i64 i, double *U, double *dU, double *dS, 
     double l = 0.0;
     for (i64 k = 0; k < deg; ++k) l += exp(U[k * H + h] - m);
     for (i64 k = 0; k < deg; ++k) U[k * H + h] = exp(U[k * H + h] - m) / l;
-    if (lse) lse[h] = deg ? m + log(l) : -INFINITY;
-    if (Y) {
-      for (int c = 0; c < dh; ++c) {
-        double y = 0.0;
-        for (i64 k = 0; k < deg; ++k) {
-          i64 j = p->indices[e0 + k];
-          y += U[k * H + h] * p->V[j * D + (i64)h * dh + c];
-        }
-        Y[(i64)h * dh + c] = y;
+    if (o->lse) o->lse[h] = deg ? m + log(l) : -INFINITY;
+    for (int c = 0; c < dh; ++c) {
+      double y = 0.0, ya = 0.0;
+      for (i64 k = 0; k < deg; ++k) {
+        i64 j = p->indices[e0 + k];
+        double v = p->V[j * (i64)H * dh + (i64)h * dh + c];
+        y += U[k * H + h] * v;
+        ya += U[k * H + h] * fabs(v);
       }
+      if (o->Y) o->Y[(i64)h * dh + c] = y;
+      if (o->Ymag) o->Ymag[(i64)h * dh + c] = ya;
     }
     if (!want_bwd) continue;
     /* softmax backward */
-    double Dsum = 0.0;
+    const i64 D = (i64)H * dh;
+    double Ds = 0.0;
     for (i64 k = 0; k < deg; ++k) {
       i64 j = p->indices[e0 + k];
       dU[k * H + h] = dot_head(p->dY + i * D + (i64)h * dh, p->V + j * D + (i64)h * dh, dh);
-      Dsum += U[k * H + h] * dU[k * H + h];
+      Ds += U[k * H + h] * dU[k * H + h];
     }
-    if (D_out) D_out[h] = Dsum;
-    for (i64 k = 0; k < deg; ++k) dS[k * H + h] = U[k * H + h] * (dU[k * H + h] - Dsum);
-    if (dB)
-      for (i64 k = 0; k < deg; ++k) dB[k * H + h] = dS[k * H + h];
-    if (dQ) {
-      for (int c = 0; c < dh; ++c) {
-        double g = 0.0;
-        for (i64 k = 0; k < deg; ++k) {
-          i64 j = p->indices[e0 + k];
-          g += dS[k * H + h] * p->K[j * D + (i64)h * dh + c];
-        }
-        dQ[(i64)h * dh + c] = p->scale * g;
+    if (o->Dsum) o->Dsum[h] = Ds;
+    for (i64 k = 0; k < deg; ++k) dS[k * H + h] = U[k * H + h] * (dU[k * H + h] - Ds);
+    if (o->dB)
+      for (i64 k = 0; k < deg; ++k) o->dB[k * H + h] = dS[k * H + h];
+    if (o->Tm)
+      for (i64 k = 0; k < deg; ++k)
+        o->Tm[k * H + h] = U[k * H + h] * (fabs(dU[k * H + h]) + fabs(Ds));
+    for (int c = 0; c < dh; ++c) {
+      double g = 0.0, ga = 0.0;
+      for (i64 k = 0; k < deg; ++k) {
+        i64 j = p->indices[e0 + k];
+        double kv = p->K[j * D + (i64)h * dh + c];
+        g += dS[k * H + h] * kv;
+        ga += U[k * H + h] * (fabs(dU[k * H + h]) + fabs(Ds)) * fabs(kv);
       }
+      if (o->dQ) o->dQ[(i64)h * dh + c] = p->scale * g;
+      if (o->dQmag) o->dQmag[(i64)h * dh + c] = p->scale * ga;
     }
   }
 }
@@ -262,10 +278,13 @@ int or_get_threads(void) {
 #define OMP_THREADS
 #endif
 
-/* Forward on every row: Y [R*D], lse [R*H]; U (nullable) [E*H]. */
+#define OFF(ptr, n) ((ptr) ? (ptr) + (n) : NULL)
+
+/* Forward on every row: Y [R*D], lse [R*H]; U (nullable) [E*H]; Ymag
+ * (nullable) [R*D]. */
 void or_fwd(i64 R, i64 M, int H, int dh, double scale, const i32 *indptr, const i32 *indices,
             const double *Q, const double *K, const double *V, const double *bias, double *Y,
-            double *lse, double *U_out) {
+            double *lse, double *U_out, double *Ymag) {
   prob_t p = {R, M, H, dh, scale, indptr, indices, Q, K, V, bias, NULL};
   const i64 D = (i64)H * dh;
   const i64 md = max_degree(indptr, R);
@@ -274,7 +293,8 @@ void or_fwd(i64 R, i64 M, int H, int dh, double scale, const i32 *indptr, const 
     double *U = (double *)malloc(sizeof(double) * (size_t)(md * H + 1));
 #pragma omp for schedule(dynamic, 64)
     for (i64 i = 0; i < R; ++i) {
-      row_pass(&p, i, U, NULL, NULL, Y + i * D, lse + i * H, NULL, NULL, NULL);
+      row_out_t o = {Y + i * D, lse + i * H, NULL, NULL, NULL, OFF(Ymag, i * D), NULL, NULL};
+      row_pass(&p, i, U, NULL, NULL, &o);
       if (U_out) memcpy(U_out + (i64)indptr[i] * H, U, sizeof(double) * (size_t)((indptr[i + 1] - indptr[i]) * H));
     }
     free(U);
@@ -282,16 +302,23 @@ void or_fwd(i64 R, i64 M, int H, int dh, double scale, const i32 *indptr, const 
 }
 
 /* Backward on the whole graph: dQ [R*D], dK, dV [M*D], dB (nullable iff bias
- * is NULL) [E*H].  Recomputes the forward row by row. */
+ * is NULL) [E*H]; the magnitudes dQmag [R*D], dKmag, dVmag [M*D] (each
+ * nullable):
+ *   dKmag[j,h,c] = scale sum_{e in column j} U_e (|dU_e| + |D_i|) |Q[i,h,c]|
+ *   dVmag[j,h,c] =       sum_{e in column j} U_e |dY[i,h,c]|.
+ * Recomputes the forward row by row. */
 void or_bwd(i64 R, i64 M, int H, int dh, double scale, const i32 *indptr, const i32 *indices,
             const double *Q, const double *K, const double *V, const double *bias, const double *dY,
-            double *dQ, double *dK, double *dV, double *dB) {
+            double *dQ, double *dK, double *dV, double *dB, double *dQmag, double *dKmag,
+            double *dVmag) {
   prob_t p = {R, M, H, dh, scale, indptr, indices, Q, K, V, bias, dY};
   const i64 D = (i64)H * dh;
   const i64 E = indptr[R];
   const i64 md = max_degree(indptr, R);
+  const int want_mag = dKmag || dVmag;
   double *Uall = (double *)malloc(sizeof(double) * (size_t)(E * H + 1));
   double *dSall = (double *)malloc(sizeof(double) * (size_t)(E * H + 1));
+  double *Tall = want_mag ? (double *)malloc(sizeof(double) * (size_t)(E * H + 1)) : NULL;
   /* row side: U, dS, dQ, dB */
 #pragma omp parallel OMP_THREADS
   {
@@ -299,8 +326,9 @@ void or_bwd(i64 R, i64 M, int H, int dh, double scale, const i32 *indptr, const 
 #pragma omp for schedule(dynamic, 64)
     for (i64 i = 0; i < R; ++i) {
       i64 e0 = indptr[i];
-      row_pass(&p, i, Uall + e0 * H, dU, dSall + e0 * H, NULL, NULL, dQ + i * D, NULL,
-               dB ? dB + e0 * H : NULL);
+      row_out_t o = {NULL, NULL, dQ + i * D, NULL, OFF(dB, e0 * H), NULL, OFF(dQmag, i * D),
+                     OFF(Tall, e0 * H)};
+      row_pass(&p, i, Uall + e0 * H, dU, dSall + e0 * H, &o);
     }
     free(dU);
   }
@@ -313,14 +341,21 @@ void or_bwd(i64 R, i64 M, int H, int dh, double scale, const i32 *indptr, const 
   for (i64 j = 0; j < M; ++j) {
     for (int h = 0; h < H; ++h) {
       for (int c = 0; c < dh; ++c) {
-        double gv = 0.0, gk = 0.0;
+        double gv = 0.0, gk = 0.0, av = 0.0, ak = 0.0;
         for (i64 t = ptr_t[j]; t < ptr_t[j + 1]; ++t) {
           i64 i = src[t], e = perm[t];
-          gv += Uall[e * H + h] * dY[i * D + (i64)h * dh + c];
-          gk += dSall[e * H + h] * Q[i * D + (i64)h * dh + c];
+          double y = dY[i * D + (i64)h * dh + c], q = Q[i * D + (i64)h * dh + c];
+          gv += Uall[e * H + h] * y;
+          gk += dSall[e * H + h] * q;
+          if (want_mag) {
+            av += Uall[e * H + h] * fabs(y);
+            ak += Tall[e * H + h] * fabs(q);
+          }
         }
         dV[j * D + (i64)h * dh + c] = gv;
         dK[j * D + (i64)h * dh + c] = scale * gk;
+        if (dVmag) dVmag[j * D + (i64)h * dh + c] = av;
+        if (dKmag) dKmag[j * D + (i64)h * dh + c] = scale * ak;
       }
     }
   }
@@ -329,13 +364,16 @@ void or_bwd(i64 R, i64 M, int H, int dh, double scale, const i32 *indptr, const 
   free(perm);
   free(Uall);
   free(dSall);
+  free(Tall);
 }
 
 /* Selected rows only: Y, lse, dQ of rows[k] into Y[k*D], lse[k*H], dQ[k*D];
- * dB (nullable) of their edges, packed row after row ([sum deg][H]). */
+ * dB (nullable) of their edges, packed row after row ([sum deg][H]);
+ * Ymag, dQmag (nullable) like Y, dQ. */
 void or_rows(i64 R, i64 M, int H, int dh, double scale, const i32 *indptr, const i32 *indices,
              const double *Q, const double *K, const double *V, const double *bias, const double *dY,
-             i64 n_sel, const i32 *rows, double *Y, double *lse, double *dQ, double *dB) {
+             i64 n_sel, const i32 *rows, double *Y, double *lse, double *dQ, double *dB,
+             double *Ymag, double *dQmag) {
   prob_t p = {R, M, H, dh, scale, indptr, indices, Q, K, V, bias, dY};
   const i64 D = (i64)H * dh;
   i64 *off = (i64 *)malloc(sizeof(i64) * (size_t)(n_sel + 1));
@@ -352,9 +390,11 @@ void or_rows(i64 R, i64 M, int H, int dh, double scale, const i32 *indptr, const
     double *dU = (double *)malloc(sizeof(double) * (size_t)(md * H + 1));
     double *dS = (double *)malloc(sizeof(double) * (size_t)(md * H + 1));
 #pragma omp for schedule(dynamic, 1)
-    for (i64 k = 0; k < n_sel; ++k)
-      row_pass(&p, rows[k], U, dU, dS, Y + k * D, lse + k * H, dQ + k * D, NULL,
-               dB ? dB + off[k] * H : NULL);
+    for (i64 k = 0; k < n_sel; ++k) {
+      row_out_t o = {Y + k * D, lse + k * H, dQ + k * D, NULL, OFF(dB, off[k] * H),
+                     OFF(Ymag, k * D), OFF(dQmag, k * D), NULL};
+      row_pass(&p, rows[k], U, dU, dS, &o);
+    }
     free(U);
     free(dU);
     free(dS);
@@ -362,12 +402,13 @@ void or_rows(i64 R, i64 M, int H, int dh, double scale, const i32 *indptr, const
   free(off);
 }
 
-/* Selected columns only: dK, dV of cols[k] into dK[k*D], dV[k*D].
- * U_e and dS_e of an in-edge come from its source row's own softmax
- * statistics (lse and D = sum U dU), computed by the same row pass. */
+/* Selected columns only: dK, dV of cols[k] into dK[k*D], dV[k*D], and their
+ * magnitudes dKmag, dVmag (nullable).  U_e and dS_e of an in-edge come from
+ * its source row's own softmax statistics (lse and D = sum U dU), computed by
+ * the same row pass. */
 void or_cols(i64 R, i64 M, int H, int dh, double scale, const i32 *indptr, const i32 *indices,
              const double *Q, const double *K, const double *V, const double *bias, const double *dY,
-             i64 n_sel, const i32 *cols, double *dK, double *dV) {
+             i64 n_sel, const i32 *cols, double *dK, double *dV, double *dKmag, double *dVmag) {
   prob_t p = {R, M, H, dh, scale, indptr, indices, Q, K, V, bias, dY};
   const i64 D = (i64)H * dh;
   const i64 E = indptr[R];
@@ -405,7 +446,10 @@ void or_cols(i64 R, i64 M, int H, int dh, double scale, const i32 *indptr, const
     double *dS = (double *)malloc(sizeof(double) * (size_t)(md * H + 1));
 #pragma omp for schedule(dynamic, 64)
     for (i64 i = 0; i < R; ++i)
-      if (need[i]) row_pass(&p, i, U, dU, dS, NULL, lse + i * H, NULL, Dr + i * H, NULL);
+      if (need[i]) {
+        row_out_t o = {NULL, lse + i * H, NULL, Dr + i * H, NULL, NULL, NULL, NULL};
+        row_pass(&p, i, U, dU, dS, &o);
+      }
     free(U);
     free(dU);
     free(dS);
@@ -415,18 +459,30 @@ void or_cols(i64 R, i64 M, int H, int dh, double scale, const i32 *indptr, const
     i64 j = cols[k];
     for (int h = 0; h < H; ++h) {
       double *gk = dK + k * D + (i64)h * dh, *gv = dV + k * D + (i64)h * dh;
-      for (int c = 0; c < dh; ++c) gk[c] = gv[c] = 0.0;
+      double *mk = OFF(dKmag, k * D + (i64)h * dh), *mv = OFF(dVmag, k * D + (i64)h * dh);
+      for (int c = 0; c < dh; ++c) {
+        gk[c] = gv[c] = 0.0;
+        if (mk) mk[c] = 0.0;
+        if (mv) mv[c] = 0.0;
+      }
       for (i64 t = cnt[k]; t < cnt[k + 1]; ++t) {
         i64 i = in_row[t], e = in_edge[t];
         double u = exp(score(&p, i, e, h) - lse[i * H + h]);
         double du = dot_head(dY + i * D + (i64)h * dh, V + j * D + (i64)h * dh, dh);
         double ds = u * (du - Dr[i * H + h]);
+        double tm = u * (fabs(du) + fabs(Dr[i * H + h]));
         for (int c = 0; c < dh; ++c) {
-          gv[c] += u * dY[i * D + (i64)h * dh + c];
-          gk[c] += ds * Q[i * D + (i64)h * dh + c];
+          double y = dY[i * D + (i64)h * dh + c], q = Q[i * D + (i64)h * dh + c];
+          gv[c] += u * y;
+          gk[c] += ds * q;
+          if (mv) mv[c] += u * fabs(y);
+          if (mk) mk[c] += tm * fabs(q);
         }
       }
-      for (int c = 0; c < dh; ++c) gk[c] *= scale;
+      for (int c = 0; c < dh; ++c) {
+        gk[c] *= scale;
+        if (mk) mk[c] *= scale;
+      }
     }
   }
   free(slot);

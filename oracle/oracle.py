@@ -54,13 +54,13 @@ def lib():
         L.or_get_threads.restype = _int
         att = [_i64, _i64, _int, _int, _dbl, _P, _P, _P, _P, _P, _P]
         L.or_fwd.restype = None
-        L.or_fwd.argtypes = att + [_P, _P, _P]
+        L.or_fwd.argtypes = att + [_P, _P, _P, _P]
         L.or_bwd.restype = None
-        L.or_bwd.argtypes = att + [_P, _P, _P, _P, _P]
+        L.or_bwd.argtypes = att + [_P, _P, _P, _P, _P, _P, _P, _P]
         L.or_rows.restype = None
-        L.or_rows.argtypes = att + [_P, _i64, _P, _P, _P, _P, _P]
+        L.or_rows.argtypes = att + [_P, _i64, _P, _P, _P, _P, _P, _P, _P]
         L.or_cols.restype = None
-        L.or_cols.argtypes = att + [_P, _i64, _P, _P, _P]
+        L.or_cols.argtypes = att + [_P, _i64, _P, _P, _P, _P, _P]
         _lib = L
     return _lib
 
@@ -135,31 +135,48 @@ def _args(indptr, indices, n_cols, Q, K, V, bias, dY, scale):
     return keep, head, (R, H, dh, ix.size)
 
 
-def fwd(indptr, indices, n_cols, Q, K, V, bias=None, scale=None, want_U=False):
-    """Y [R,H,dh], lse [R,H] (and U [E,H] if want_U), all float64."""
+def _mag(mag, name, shape):
+    if mag is None:
+        return None
+    mag[name] = np.empty(shape, np.float64)
+    return mag[name]
+
+
+def fwd(indptr, indices, n_cols, Q, K, V, bias=None, scale=None, want_U=False, mag=None):
+    """Y [R,H,dh], lse [R,H] (and U [E,H] if want_U), all float64.
+
+    If ``mag`` is a dict, mag["Y"] gets sum_e U_e |V_j|, the sum of the
+    absolute values of the terms of Y (the conditioning of that sum)."""
     scale = Q.shape[2] ** -0.5 if scale is None else scale
     keep, head, (R, H, dh, E) = _args(indptr, indices, n_cols, Q, K, V, bias, None, scale)
     Y = np.empty((R, H, dh), np.float64)
     lse = np.empty((R, H), np.float64)
     U = np.empty((E, H), np.float64) if want_U else None
-    lib().or_fwd(*head, _p(Y), _p(lse), _p(U))
+    lib().or_fwd(*head, _p(Y), _p(lse), _p(U), _p(_mag(mag, "Y", (R, H, dh))))
     return (Y, lse, U) if want_U else (Y, lse)
 
 
-def bwd(indptr, indices, n_cols, Q, K, V, dY, bias=None, scale=None):
-    """dQ [R,H,dh], dK, dV [M,H,dh], dB [E,H] (None without bias), float64."""
+def bwd(indptr, indices, n_cols, Q, K, V, dY, bias=None, scale=None, mag=None):
+    """dQ [R,H,dh], dK, dV [M,H,dh], dB [E,H] (None without bias), float64.
+
+    If ``mag`` is a dict, mag["dQ"], mag["dK"], mag["dV"] get the sums of the
+    absolute values of the terms of each output, with the score gradient
+    U (dU - D) of a term bounded by U (|dU| + |D|)."""
     scale = Q.shape[2] ** -0.5 if scale is None else scale
     keep, head, (R, H, dh, E) = _args(indptr, indices, n_cols, Q, K, V, bias, dY, scale)
     dQ = np.empty((R, H, dh), np.float64)
     dK = np.empty((n_cols, H, dh), np.float64)
     dV = np.empty((n_cols, H, dh), np.float64)
     dB = np.empty((E, H), np.float64) if bias is not None else None
-    lib().or_bwd(*head, _p(keep[6]), _p(dQ), _p(dK), _p(dV), _p(dB))
+    lib().or_bwd(*head, _p(keep[6]), _p(dQ), _p(dK), _p(dV), _p(dB),
+                 _p(_mag(mag, "dQ", (R, H, dh))), _p(_mag(mag, "dK", (n_cols, H, dh))),
+                 _p(_mag(mag, "dV", (n_cols, H, dh))))
     return dQ, dK, dV, dB
 
 
-def rows(indptr, indices, n_cols, Q, K, V, dY, sel, bias=None, scale=None):
-    """Y, lse, dQ of the rows ``sel`` and dB of their edges (packed)."""
+def rows(indptr, indices, n_cols, Q, K, V, dY, sel, bias=None, scale=None, mag=None):
+    """Y, lse, dQ of the rows ``sel`` and dB of their edges (packed); with a
+    ``mag`` dict, mag["Y"] and mag["dQ"] of those rows."""
     scale = Q.shape[2] ** -0.5 if scale is None else scale
     keep, head, (R, H, dh, E) = _args(indptr, indices, n_cols, Q, K, V, bias, dY, scale)
     sel = _i32a(sel)
@@ -169,16 +186,19 @@ def rows(indptr, indices, n_cols, Q, K, V, dY, sel, bias=None, scale=None):
     lse = np.empty((sel.size, H), np.float64)
     dQ = np.empty((sel.size, H, dh), np.float64)
     dB = np.empty((n_e, H), np.float64) if bias is not None else None
-    lib().or_rows(*head, _p(keep[6]), sel.size, _p(sel), _p(Y), _p(lse), _p(dQ), _p(dB))
+    lib().or_rows(*head, _p(keep[6]), sel.size, _p(sel), _p(Y), _p(lse), _p(dQ), _p(dB),
+                  _p(_mag(mag, "Y", Y.shape)), _p(_mag(mag, "dQ", dQ.shape)))
     return Y, lse, dQ, dB
 
 
-def cols(indptr, indices, n_cols, Q, K, V, dY, sel, bias=None, scale=None):
-    """dK, dV of the columns ``sel``."""
+def cols(indptr, indices, n_cols, Q, K, V, dY, sel, bias=None, scale=None, mag=None):
+    """dK, dV of the columns ``sel``; with a ``mag`` dict, mag["dK"] and
+    mag["dV"] of those columns."""
     scale = Q.shape[2] ** -0.5 if scale is None else scale
     keep, head, (R, H, dh, E) = _args(indptr, indices, n_cols, Q, K, V, bias, dY, scale)
     sel = _i32a(sel)
     dK = np.empty((sel.size, H, dh), np.float64)
     dV = np.empty((sel.size, H, dh), np.float64)
-    lib().or_cols(*head, _p(keep[6]), sel.size, _p(sel), _p(dK), _p(dV))
+    lib().or_cols(*head, _p(keep[6]), sel.size, _p(sel), _p(dK), _p(dV),
+                  _p(_mag(mag, "dK", dK.shape)), _p(_mag(mag, "dV", dV.shape)))
     return dK, dV

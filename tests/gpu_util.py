@@ -2,9 +2,16 @@
 parity comparison.
 
 Tolerance (fp32 1e-5, bf16 inputs with fp32 accumulation 2e-2, both
-relative): per tensor and head, |got - ref| <= rtol*|ref| + rtol*rms(ref)
-elementwise, where rms is over the head's compared elements; lse compares as
-|got - ref| <= rtol*max(1, |ref|), and -inf (empty rows) must match exactly.
+relative), per tensor and head:
+  * the relative error ||got - ref||_2 / ||ref||_2 <= rtol, and
+  * elementwise |got - ref| <= rtol*|ref| + rtol*rms(ref) + 8*u*mag, where
+    rms is over the head's compared elements, u = 2^-24 is the unit roundoff
+    of the float32 arithmetic, and mag (from the oracle) is the sum of the
+    absolute values of the terms that define the element: a sum whose terms
+    cancel (mag >> |ref|) cannot be computed in float32 to better than about
+    u*mag, whatever the order of summation.
+lse compares as |got - ref| <= rtol*max(1, |ref|), and -inf (empty rows) must
+match exactly.
 """
 import numpy as np
 import torch
@@ -26,7 +33,10 @@ def to_np(t):
     return t.detach().float().cpu().numpy().astype(np.float64)
 
 
-def assert_close(got, ref, rtol, name):
+U32 = 2.0 ** -24
+
+
+def assert_close(got, ref, rtol, name, mag=None):
     g = got if isinstance(got, np.ndarray) else to_np(got)
     ref = np.asarray(ref, np.float64)
     assert g.shape == ref.shape, (name, g.shape, ref.shape)
@@ -34,7 +44,13 @@ def assert_close(got, ref, rtol, name):
         return
     axes = tuple(a for a in range(ref.ndim) if a != 1) if ref.ndim >= 2 else (0,)
     rms = np.sqrt(np.mean(ref ** 2, axis=axes, keepdims=True))
+    d2 = np.sqrt(np.sum((g - ref) ** 2, axis=axes))
+    r2 = np.sqrt(np.sum(ref ** 2, axis=axes))
+    ok = (d2 <= rtol * r2) | (r2 == 0)       # an all-zero reference is left to the elementwise bound
+    assert np.all(ok), f"{name}: relative L2 error {d2 / np.maximum(r2, 1e-300)} > {rtol}"
     bound = rtol * np.abs(ref) + rtol * rms
+    if mag is not None:
+        bound = bound + 8 * U32 * np.asarray(mag, np.float64)
     err = np.abs(g - ref)
     bad = ~(err <= bound)
     if bad.any():

@@ -35,13 +35,14 @@ def check_full(P, out, rtol=None):
     rtol = RTOL[P.cfg.dtype] if rtol is None else rtol
     Y, lse, dQ, dK, dV, dB = out
     M = P.cfg.n_cols
-    rY, rl = O.fwd(P.indptr, P.indices, M, P.Q, P.K, P.V, P.bias, P.scale)
-    rQ, rK, rV, rB = O.bwd(P.indptr, P.indices, M, P.Q, P.K, P.V, P.dY, P.bias, P.scale)
-    assert_close(Y, rY, rtol, "Y")
+    m = {}
+    rY, rl = O.fwd(P.indptr, P.indices, M, P.Q, P.K, P.V, P.bias, P.scale, mag=m)
+    rQ, rK, rV, rB = O.bwd(P.indptr, P.indices, M, P.Q, P.K, P.V, P.dY, P.bias, P.scale, mag=m)
+    assert_close(Y, rY, rtol, "Y", m["Y"])
     assert_lse(lse, rl, 1e-5 if P.cfg.dtype == "f32" else 1e-4)
-    assert_close(dQ, rQ, rtol, "dQ")
-    assert_close(dK, rK, rtol, "dK")
-    assert_close(dV, rV, rtol, "dV")
+    assert_close(dQ, rQ, rtol, "dQ", m["dQ"])
+    assert_close(dK, rK, rtol, "dK", m["dK"])
+    assert_close(dV, rV, rtol, "dV", m["dV"])
     if P.bias is not None:
         assert_close(dB, rB, rtol, "dbias")
     else:

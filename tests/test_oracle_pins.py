@@ -446,3 +446,52 @@ def test_schedule_definition(ts, tm, ch):
         k += nch
     assert k == len(items)
     np.testing.assert_array_equal(S["merges"].reshape(-1, 3), np.array(merges, np.int32).reshape(-1, 3))
+
+
+# ----------------------------------------------------------------------------
+# term magnitudes (the conditioning used by the GPU tolerance)
+# ----------------------------------------------------------------------------
+
+def test_magnitudes():
+    """Y and dV are linear in V and dY with nonnegative weights, so their term
+    magnitudes equal the oracle's own Y and dV on |V| and |dY|; the dQ and dK
+    magnitudes match a dense computation from torch's masked softmax, and
+    every magnitude bounds its value."""
+    R, M, H, dh = 40, 50, 2, 8
+    degs = np.random.default_rng(13).integers(0, 20, R)
+    P = _rand_problem(60, R, M, H, dh, degs, bias=True, self_loops=False)
+    m = {}
+    Y, _ = O.fwd(P.indptr, P.indices, M, P.Q, P.K, P.V, P.bias, mag=m)
+    Ya, _ = O.fwd(P.indptr, P.indices, M, P.Q, P.K, np.abs(P.V), P.bias)
+    _close(m["Y"], Ya, 1e-14)
+    assert np.all(m["Y"] >= np.abs(Y) - 1e-14)
+    mb = {}
+    dQ, dK, dV, _ = O.bwd(P.indptr, P.indices, M, P.Q, P.K, P.V, P.dY, P.bias, mag=mb)
+    _, _, dVa, _ = O.bwd(P.indptr, P.indices, M, P.Q, P.K, P.V, np.abs(P.dY), P.bias)
+    _close(mb["dV"], dVa, 1e-14)
+    for g, a in ((dQ, mb["dQ"]), (dK, mb["dK"]), (dV, mb["dV"])):
+        assert np.all(a >= np.abs(g) - 1e-12)
+    # dense: U from torch's masked softmax, T = U (|dU| + |D|)
+    rows = np.repeat(np.arange(R), np.diff(P.indptr))
+    q, k, v, dy = (torch.tensor(x, dtype=torch.float64).permute(1, 0, 2) for x in (P.Q, P.K, P.V, P.dY))
+    s = torch.full((H, R, M), float("-inf"), dtype=torch.float64)
+    s[:, rows, P.indices] = P.scale * (q[:, rows] * k[:, P.indices]).sum(-1) + torch.tensor(P.bias.T)
+    U = torch.nan_to_num(torch.softmax(s, dim=-1), nan=0.0)
+    dU = dy @ v.transpose(1, 2)
+    Dr = (U * dU).sum(-1, keepdim=True)
+    T = U * (dU.abs() + Dr.abs())
+    dQm = P.scale * (T @ k.abs())
+    dKm = P.scale * (T.transpose(1, 2) @ q.abs())
+    _close(mb["dQ"], dQm.permute(1, 0, 2).numpy(), 1e-12)
+    _close(mb["dK"], dKm.permute(1, 0, 2).numpy(), 1e-12)
+    # the per-row / per-column entry points give the same magnitudes
+    sel = np.array([3, 0, 39], np.int32)
+    mr = {}
+    O.rows(P.indptr, P.indices, M, P.Q, P.K, P.V, P.dY, sel, P.bias, mag=mr)
+    _close(mr["Y"], m["Y"][sel], 1e-14)
+    _close(mr["dQ"], mb["dQ"][sel], 1e-14)
+    cs = np.array([7, 49, 0], np.int32)
+    mc = {}
+    O.cols(P.indptr, P.indices, M, P.Q, P.K, P.V, P.dY, cs, P.bias, mag=mc)
+    _close(mc["dK"], mb["dK"][cs], 1e-13)
+    _close(mc["dV"], mb["dV"][cs], 1e-13)
