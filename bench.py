@@ -84,17 +84,22 @@ def cpu_baseline(P, budget_s: float):
     size is picked so the run takes about budget_s seconds."""
     from oracle import oracle as O
     cfg = P.cfg
+    # the oracle works in float64: widen the inputs once, outside the timing
+    Q, K, V, dY = (np.ascontiguousarray(x, dtype=np.float64) for x in (P.Q, P.K, P.V, P.dY))
+    B = None if P.bias is None else np.ascontiguousarray(P.bias, dtype=np.float64)
+
     # calibrate on a small row block, then size the measured block
     def block(k):
         ip = P.indptr[: k + 1]
         e = int(ip[-1])
-        return ip, P.indices[:e], (P.bias[:e] if P.bias is not None else None), e
+        return ip, P.indices[:e], (B[:e] if B is not None else None), e
 
     def run(k):
         ip, ix, bias, e = block(k)
+        q, dy = np.ascontiguousarray(Q[:k]), np.ascontiguousarray(dY[:k])
         t = time.perf_counter()
-        O.fwd(ip, ix, cfg.n_cols, P.Q[:k], P.K, P.V, bias, P.scale)
-        O.bwd(ip, ix, cfg.n_cols, P.Q[:k], P.K, P.V, P.dY[:k], bias, P.scale)
+        O.fwd(ip, ix, cfg.n_cols, q, K, V, bias, P.scale)
+        O.bwd(ip, ix, cfg.n_cols, q, K, V, dy, bias, P.scale)
         return time.perf_counter() - t, e
 
     R = cfg.n_rows
@@ -127,7 +132,20 @@ def main():
                     choices=["tiny", "mid", "large", "hub", "shard"])
     ap.add_argument("--cpu-budget", type=float, default=15.0,
                     help="seconds of oracle work for the CPU baseline (0: skip)")
+    ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
+                    help="only run a plain device-to-device copy of MIB MiB, 5 times "
+                         "(calibrates the HBM byte counters against a known size)")
     args = ap.parse_args()
+    if args.copy_probe:
+        import torch
+        n = args.copy_probe << 20
+        src = torch.ones(n, dtype=torch.uint8, device="cuda:0")
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_probe_bytes": n, "launches": 5}))
+        return
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported "
               "(the multi-GPU sharding is described, not built)", file=sys.stderr)

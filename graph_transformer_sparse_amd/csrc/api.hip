@@ -19,7 +19,7 @@ namespace gt {
 bool shape_supported(gt_dtype dt, int heads, int head_dim);
 gt_status launch_fwd(const gt_graph *g, int heads, int head_dim, gt_dtype dt, float scale,
                      const void *Q, const void *K, const void *V, const float *bias, void *Y,
-                     float *lse, float *part_ml, float *part_acc, hipStream_t st);
+                     float *lse, float *part, hipStream_t st);
 gt_status launch_bwd(const gt_graph *g, int heads, int head_dim, gt_dtype dt, float scale,
                      const void *Q, const void *K, const void *V, const float *bias,
                      const float *lse, const void *dY, void *dQ, void *dK,
@@ -89,7 +89,7 @@ using namespace gt;
 namespace {
 
 struct WorkLayout {
-  size_t part_ml, part_acc;               // forward
+  size_t part_fwd;                        // forward
   size_t rowstat, part_rows, part_cols;   // backward
   size_t fwd_total, bwd_total, total;
 };
@@ -100,13 +100,12 @@ WorkLayout work_layout(const gt_graph *g, int heads, int head_dim) {
   WorkLayout w;
   const size_t D = (size_t)heads * head_dim;
   const size_t sr = (size_t)g->rows.n_items, sc = (size_t)g->cols.n_items;
-  w.part_ml = 0;
-  w.part_acc = align256(sr * heads * 2 * sizeof(float));
-  w.fwd_total = w.part_acc + align256(sr * D * sizeof(float));
+  w.part_fwd = 0;
+  w.fwd_total = align256(sr * (size_t)fwd_slot_floats(D, heads) * sizeof(float));
   w.rowstat = 0;
   w.part_rows = align256((size_t)g->n_rows * heads * 2 * sizeof(float));
-  w.part_cols = w.part_rows + align256(sr * (2 * D + 3 * heads) * sizeof(float));
-  w.bwd_total = w.part_cols + align256(sc * 2 * D * sizeof(float));
+  w.part_cols = w.part_rows + align256(sr * (size_t)rows_slot_floats(D, heads) * sizeof(float));
+  w.bwd_total = w.part_cols + align256(sc * (size_t)cols_slot_floats(D, heads) * sizeof(float));
   w.total = std::max<size_t>(std::max(w.fwd_total, w.bwd_total), 256);
   return w;
 }
@@ -168,7 +167,7 @@ extern "C" gt_status gt_attn_fwd(const gt_graph *g, int32_t heads, int32_t head_
     return fail(GT_E_WORKSPACE, "work has %zu bytes, needs %zu", work_bytes, w.fwd_total);
   char *wb = (char *)work;
   return launch_fwd(g, heads, head_dim, dt, scale, Q, K, V, bias, Y, lse,
-                    (float *)(wb + w.part_ml), (float *)(wb + w.part_acc), (hipStream_t)stream);
+                    (float *)(wb + w.part_fwd), (hipStream_t)stream);
 }
 
 extern "C" gt_status gt_attn_bwd(const gt_graph *g, int32_t heads, int32_t head_dim, gt_dtype dt,

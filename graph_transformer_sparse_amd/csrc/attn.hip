@@ -115,6 +115,181 @@ __device__ inline void merge_weights(float m, float mo, float &mn, float &fa, fl
 }
 
 // ---------------------------------------------------------------------------
+// Per-pass partial states.  A state is one lane's share of a segment's
+// partial result: vectors over the lane's N channels and per-head scalars
+// (equal on the HL lanes of a head).  merge() folds another state in, in a
+// fixed order; xor_lane() fetches a partner lane's state; put()/get() move
+// it to / from a piece slot (layouts in layout.hpp).
+// ---------------------------------------------------------------------------
+template <int N> struct FwdState {
+  float m, l, acc[N];
+  __device__ void init() {
+    m = -INFINITY;
+    l = 0.f;
+#pragma unroll
+    for (int c = 0; c < N; ++c) acc[c] = 0.f;
+  }
+  __device__ void merge(const FwdState &o) {
+    float mn, fa, fb;
+    merge_weights(m, o.m, mn, fa, fb);
+    l = l * fa + o.l * fb;
+#pragma unroll
+    for (int c = 0; c < N; ++c) acc[c] = acc[c] * fa + o.acc[c] * fb;
+    m = mn;
+  }
+  __device__ FwdState xor_lane(int off) const {
+    FwdState o;
+    o.m = __shfl_xor(m, off);
+    o.l = __shfl_xor(l, off);
+#pragma unroll
+    for (int c = 0; c < N; ++c) o.acc[c] = __shfl_xor(acc[c], off);
+    return o;
+  }
+  template <int D, int H> __device__ void put(float *slot, int gl, int h, bool head_lane) const {
+#pragma unroll
+    for (int c = 0; c < N; c += 4)
+      *reinterpret_cast<float4 *>(slot + gl * N + c) = make_float4(acc[c], acc[c + 1], acc[c + 2], acc[c + 3]);
+    if (head_lane) {
+      slot[D + h] = m;
+      slot[D + H + h] = l;
+    }
+  }
+  template <int D, int H> __device__ void get(const float *slot, int gl, int h) {
+#pragma unroll
+    for (int c = 0; c < N; c += 4) {
+      const float4 v = *reinterpret_cast<const float4 *>(slot + gl * N + c);
+      acc[c] = v.x; acc[c + 1] = v.y; acc[c + 2] = v.z; acc[c + 3] = v.w;
+    }
+    m = slot[D + h];
+    l = slot[D + H + h];
+  }
+};
+
+// Backward row pass (see the comment above k_bwd_rows).
+template <int N> struct RowState {
+  float a1[N], a2[N], s, l, c;
+  __device__ void init() {
+    s = l = c = 0.f;
+#pragma unroll
+    for (int k = 0; k < N; ++k) a1[k] = a2[k] = 0.f;
+  }
+  // this (+)= o at this state's shift, unless this one is empty
+  __device__ void merge(const RowState &o) {
+    if (l == 0.f) {
+      *this = o;
+      return;
+    }
+    const float dc = o.c - c;
+    s += o.s + dc * o.l;
+    l += o.l;
+#pragma unroll
+    for (int k = 0; k < N; ++k) {
+      a1[k] += o.a1[k] + dc * o.a2[k];
+      a2[k] += o.a2[k];
+    }
+  }
+  __device__ RowState xor_lane(int off) const {
+    RowState o;
+    o.s = __shfl_xor(s, off);
+    o.l = __shfl_xor(l, off);
+    o.c = __shfl_xor(c, off);
+#pragma unroll
+    for (int k = 0; k < N; ++k) {
+      o.a1[k] = __shfl_xor(a1[k], off);
+      o.a2[k] = __shfl_xor(a2[k], off);
+    }
+    return o;
+  }
+  template <int D, int H> __device__ void put(float *slot, int gl, int h, bool head_lane) const {
+#pragma unroll
+    for (int k = 0; k < N; k += 4) {
+      *reinterpret_cast<float4 *>(slot + gl * N + k) = make_float4(a1[k], a1[k + 1], a1[k + 2], a1[k + 3]);
+      *reinterpret_cast<float4 *>(slot + D + gl * N + k) = make_float4(a2[k], a2[k + 1], a2[k + 2], a2[k + 3]);
+    }
+    if (head_lane) {
+      slot[2 * D + h] = s;
+      slot[2 * D + H + h] = l;
+      slot[2 * D + 2 * H + h] = c;
+    }
+  }
+  template <int D, int H> __device__ void get(const float *slot, int gl, int h) {
+#pragma unroll
+    for (int k = 0; k < N; k += 4) {
+      const float4 x = *reinterpret_cast<const float4 *>(slot + gl * N + k);
+      const float4 y = *reinterpret_cast<const float4 *>(slot + D + gl * N + k);
+      a1[k] = x.x; a1[k + 1] = x.y; a1[k + 2] = x.z; a1[k + 3] = x.w;
+      a2[k] = y.x; a2[k + 1] = y.y; a2[k + 2] = y.z; a2[k + 3] = y.w;
+    }
+    s = slot[2 * D + h];
+    l = slot[2 * D + H + h];
+    c = slot[2 * D + 2 * H + h];
+  }
+};
+
+// Backward column pass: plain sums of the dK and dV terms.
+template <int N> struct ColState {
+  float k[N], v[N];
+  __device__ void init() {
+#pragma unroll
+    for (int c = 0; c < N; ++c) k[c] = v[c] = 0.f;
+  }
+  __device__ void merge(const ColState &o) {
+#pragma unroll
+    for (int c = 0; c < N; ++c) {
+      k[c] += o.k[c];
+      v[c] += o.v[c];
+    }
+  }
+  __device__ ColState xor_lane(int off) const {
+    ColState o;
+#pragma unroll
+    for (int c = 0; c < N; ++c) {
+      o.k[c] = __shfl_xor(k[c], off);
+      o.v[c] = __shfl_xor(v[c], off);
+    }
+    return o;
+  }
+  template <int D, int H> __device__ void put(float *slot, int gl, int, bool) const {
+#pragma unroll
+    for (int c = 0; c < N; c += 4) {
+      *reinterpret_cast<float4 *>(slot + gl * N + c) = make_float4(k[c], k[c + 1], k[c + 2], k[c + 3]);
+      *reinterpret_cast<float4 *>(slot + D + gl * N + c) = make_float4(v[c], v[c + 1], v[c + 2], v[c + 3]);
+    }
+  }
+  template <int D, int H> __device__ void get(const float *slot, int gl, int) {
+#pragma unroll
+    for (int c = 0; c < N; c += 4) {
+      const float4 x = *reinterpret_cast<const float4 *>(slot + gl * N + c);
+      const float4 y = *reinterpret_cast<const float4 *>(slot + D + gl * N + c);
+      k[c] = x.x; k[c + 1] = x.y; k[c + 2] = x.z; k[c + 3] = x.w;
+      v[c] = y.x; v[c + 1] = y.y; v[c + 2] = y.z; v[c + 3] = y.w;
+    }
+  }
+};
+
+// Fold the lane groups of a wavefront into group 0 by a fixed butterfly
+// (group g first meets g ^ 1, then g ^ 2, ...).
+template <class S, int G> __device__ inline void wave_combine(S &st) {
+#pragma unroll
+  for (int off = G; off < WAVE; off <<= 1) {
+    const S o = st.xor_lane(off);
+    st.merge(o);
+  }
+}
+
+// The edge ids e, e + step, ... of one round, clamped to the round's first
+// (valid) edge past the segment end, and the values idx holds there.
+template <int U>
+__device__ inline void round_ids(const int32_t *idx, int64_t e, int64_t ee, int step,
+                                 int32_t (&v)[U]) {
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    const int64_t eu = e + (int64_t)u * step;
+    v[u] = idx[eu < ee ? eu : e];
+  }
+}
+
+// ---------------------------------------------------------------------------
 // forward
 // ---------------------------------------------------------------------------
 struct FwdArgs {
@@ -124,10 +299,21 @@ struct FwdArgs {
   const float *bias;
   void *Y;
   float *lse;
-  float *part_ml;   // [slots][H][2]  (m2, l) of split-row pieces
-  float *part_acc;  // [slots][D]
+  float *part;      // [slots][fwd_slot_floats] states of split-row pieces
   float qscale;     // scale * log2(e)
 };
+
+template <typename T, int HL, int H>
+__device__ inline void finish_fwd(const FwdArgs &a, int64_t row, int gl, int h,
+                                  const FwdState<Vec<T>::N> &st) {
+  constexpr int N = Vec<T>::N, D = HL * H * N;
+  const float inv = st.l > 0.f ? 1.f / st.l : 0.f;
+  float y[N];
+#pragma unroll
+  for (int c = 0; c < N; ++c) y[c] = st.acc[c] * inv;
+  Vec<T>::store((T *)a.Y + row * D + gl * N, y);
+  if (gl % HL == 0) a.lse[row * H + h] = st.l > 0.f ? (st.m + fast_log2(st.l)) * LN2 : -INFINITY;
+}
 
 template <typename T, int HL, int H, int U, bool BIAS>
 __global__ __launch_bounds__(BLOCK) void k_fwd(FwdArgs a) {
@@ -135,24 +321,25 @@ __global__ __launch_bounds__(BLOCK) void k_fwd(FwdArgs a) {
   const int lane = threadIdx.x & (WAVE - 1), grp = lane / G, gl = lane % G, h = gl / HL;
   const Work wk = decode<RPW>(a.s, grp);
   if (!wk.active) return;
-  const T *Qp = (const T *)a.Q, *Kp = (const T *)a.K, *Vp = (const T *)a.V;
+  const T *Kp = (const T *)a.K, *Vp = (const T *)a.V;
   const int64_t row = wk.seg;
   float q[N];
-  Vec<T>::load(Qp + row * D + gl * N, q);
+  Vec<T>::load((const T *)a.Q + row * D + gl * N, q);
 #pragma unroll
   for (int c = 0; c < N; ++c) q[c] *= a.qscale;
-  float m = -INFINITY, l = 0.f, acc[N];
-#pragma unroll
-  for (int c = 0; c < N; ++c) acc[c] = 0.f;
-  const int gstart = wk.wave_item ? grp : 0, gstep = wk.wave_item ? RPW : 1;
-  for (int64_t e = (int64_t)wk.eb + gstart; e < wk.ee; e += (int64_t)gstep * U) {
+  FwdState<N> st;
+  st.init();
+  const int gstep = wk.wave_item ? RPW : 1;
+  int64_t e = (int64_t)wk.eb + (wk.wave_item ? grp : 0);
+  int32_t jn[U];
+  if (e < wk.ee) round_ids<U>(a.idx, e, wk.ee, gstep, jn);
+  for (; e < wk.ee; e += (int64_t)gstep * U) {
     int32_t j[U];
     bool ok[U];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      const int64_t eu = e + (int64_t)u * gstep;
-      ok[u] = eu < wk.ee;
-      j[u] = a.idx[ok[u] ? eu : e];
+      j[u] = jn[u];
+      ok[u] = e + (int64_t)u * gstep < wk.ee;
     }
     typename Raw<T>::type kr[U], vr[U];
 #pragma unroll
@@ -167,8 +354,10 @@ __global__ __launch_bounds__(BLOCK) void k_fwd(FwdArgs a) {
         b[u] = a.bias[(ok[u] ? eu : e) * H + h] * LOG2E;
       }
     }
+    const int64_t en = e + (int64_t)gstep * U;   // prefetch the next round's columns
+    if (en < wk.ee) round_ids<U>(a.idx, en, wk.ee, gstep, jn);
     float sc[U];
-    float mn = m;
+    float mn = st.m;
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       float kx[N];
@@ -181,81 +370,76 @@ __global__ __launch_bounds__(BLOCK) void k_fwd(FwdArgs a) {
       sc[u] = ok[u] ? d : -INFINITY;
       mn = fmaxf(mn, sc[u]);
     }
-    const float alpha = fast_exp2(m - mn);
-    l *= alpha;
+    const float alpha = fast_exp2(st.m - mn);
+    st.l *= alpha;
 #pragma unroll
-    for (int c = 0; c < N; ++c) acc[c] *= alpha;
+    for (int c = 0; c < N; ++c) st.acc[c] *= alpha;
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const float p = fast_exp2(sc[u] - mn);
       float vx[N];
       unpack(vr[u], vx);
-      l += p;
+      st.l += p;
 #pragma unroll
-      for (int c = 0; c < N; ++c) acc[c] = fmaf(p, vx[c], acc[c]);
+      for (int c = 0; c < N; ++c) st.acc[c] = fmaf(p, vx[c], st.acc[c]);
     }
-    m = mn;
+    st.m = mn;
   }
   if (wk.wave_item) {
-#pragma unroll
-    for (int off = G; off < WAVE; off <<= 1) {
-      const float mo = __shfl_xor(m, off), lo = __shfl_xor(l, off);
-      float mn, fa, fb;
-      merge_weights(m, mo, mn, fa, fb);
-      l = l * fa + lo * fb;
-#pragma unroll
-      for (int c = 0; c < N; ++c) acc[c] = acc[c] * fa + __shfl_xor(acc[c], off) * fb;
-      m = mn;
-    }
+    wave_combine<FwdState<N>, G>(st);
     if (grp != 0) return;
     if (wk.slot >= 0) {
-      float *pa = a.part_acc + (int64_t)wk.slot * D + gl * N;
-#pragma unroll
-      for (int c = 0; c < N; c += 4)
-        *reinterpret_cast<float4 *>(pa + c) = make_float4(acc[c], acc[c + 1], acc[c + 2], acc[c + 3]);
-      if (gl % HL == 0)
-        *reinterpret_cast<float2 *>(a.part_ml + ((int64_t)wk.slot * H + h) * 2) = make_float2(m, l);
+      st.template put<D, H>(a.part + (int64_t)wk.slot * fwd_slot_floats(D, H), gl, h, gl % HL == 0);
       return;
     }
   }
-  const float inv = l > 0.f ? 1.f / l : 0.f;
-  float y[N];
-#pragma unroll
-  for (int c = 0; c < N; ++c) y[c] = acc[c] * inv;
-  Vec<T>::store((T *)a.Y + row * D + gl * N, y);
-  if (gl % HL == 0) a.lse[row * H + h] = l > 0.f ? (m + fast_log2(l)) * LN2 : -INFINITY;
+  finish_fwd<T, HL, H>(a, row, gl, h, st);
 }
 
-// One wavefront per split row: merge its pieces' states in piece order.
+// ---------------------------------------------------------------------------
+// merge of split segments: one workgroup per segment; lane group g of the
+// workgroup folds in pieces g, g + NG, g + 2 NG, ... (NG groups), then the
+// groups are folded by the butterfly inside each wavefront and the
+// wavefronts in order through LDS.  Returns true on the one group holding
+// the result (wavefront 0, group 0).
+// ---------------------------------------------------------------------------
+template <class S, int D, int H, int G, int64_t SLOT>
+__device__ inline bool merge_pieces(S &st, const float *part, int64_t first, int64_t nch, int wv,
+                                    int grp, int gl, int h) {
+  constexpr int RPW = WAVE / G, NG = WPB * RPW, UNR = 4;
+  __shared__ S lds[WPB * G];
+  const int gid = wv * RPW + grp;
+  st.init();
+  for (int64_t k = gid; k < nch; k += (int64_t)NG * UNR) {
+    S o[UNR];
+#pragma unroll
+    for (int q = 0; q < UNR; ++q) {
+      const int64_t kk = k + (int64_t)q * NG;
+      if (kk < nch) o[q].template get<D, H>(part + (first + kk) * SLOT, gl, h);
+      else o[q].init();
+    }
+#pragma unroll
+    for (int q = 0; q < UNR; ++q) st.merge(o[q]);
+  }
+  wave_combine<S, G>(st);
+  if (grp == 0) lds[wv * G + gl] = st;
+  __syncthreads();
+  if (wv != 0 || grp != 0) return false;
+#pragma unroll
+  for (int w = 1; w < WPB; ++w) st.merge(lds[w * G + gl]);
+  return true;
+}
+
 template <typename T, int HL, int H>
 __global__ __launch_bounds__(BLOCK) void k_fwd_merge(FwdArgs a) {
   constexpr int N = Vec<T>::N, G = HL * H, D = G * N;
-  const int64_t w = (int64_t)blockIdx.x * WPB + threadIdx.x / WAVE;
-  const int lane = threadIdx.x & (WAVE - 1);
-  if (w >= a.s.n_merges || lane >= G) return;
-  const int gl = lane, h = gl / HL;
-  const int32_t *rec = a.s.merges + 3 * w;
+  const int lane = threadIdx.x & (WAVE - 1), grp = lane / G, gl = lane % G, h = gl / HL;
+  const int32_t *rec = a.s.merges + 3 * (int64_t)blockIdx.x;
   const int64_t row = rec[0], first = rec[1], nch = rec[2];
-  float m = -INFINITY, l = 0.f, acc[N];
-#pragma unroll
-  for (int c = 0; c < N; ++c) acc[c] = 0.f;
-  for (int64_t k = 0; k < nch; ++k) {
-    const int64_t slot = first + k;
-    const float2 ml = *reinterpret_cast<const float2 *>(a.part_ml + (slot * H + h) * 2);
-    const float *pa = a.part_acc + slot * D + gl * N;
-    float mn, fa, fb;
-    merge_weights(m, ml.x, mn, fa, fb);
-    l = l * fa + ml.y * fb;
-#pragma unroll
-    for (int c = 0; c < N; ++c) acc[c] = acc[c] * fa + pa[c] * fb;
-    m = mn;
-  }
-  const float inv = l > 0.f ? 1.f / l : 0.f;
-  float y[N];
-#pragma unroll
-  for (int c = 0; c < N; ++c) y[c] = acc[c] * inv;
-  Vec<T>::store((T *)a.Y + row * D + gl * N, y);
-  if (gl % HL == 0) a.lse[row * H + h] = l > 0.f ? (m + fast_log2(l)) * LN2 : -INFINITY;
+  FwdState<N> st;
+  if (merge_pieces<FwdState<N>, D, H, G, fwd_slot_floats(D, H)>(st, a.part, first, nch,
+                                                                threadIdx.x / WAVE, grp, gl, h))
+    finish_fwd<T, HL, H>(a, row, gl, h, st);
 }
 
 // ---------------------------------------------------------------------------
@@ -284,32 +468,10 @@ struct BwdArgs {
   void *dQ, *dK, *dV;
   float *dbias;
   float2 *rowstat;        // [R][H] (lse * log2(e) + log2(L), D)
-  float *part_rows;       // [slots][2D + 3H]: A1, A2, S, L, c of split-row pieces
-  float *part_cols;       // [slots][2D]: dK partial, then dV partial
+  float *part_rows;       // [slots][rows_slot_floats] states of split-row pieces
+  float *part_cols;       // [slots][cols_slot_floats] states of split-column pieces
   float qscale, scale;
 };
-
-// Row-pass state of one lane: its N channels of A1 and A2, and the per-head
-// L, S and shift c (equal on the HL lanes of a head).
-template <int N> struct RowState {
-  float a1[N], a2[N], s, l, c;
-};
-
-// st (+)= o, at the shift of st unless st is empty.
-template <int N> __device__ inline void row_merge(RowState<N> &st, const RowState<N> &o) {
-  if (st.l == 0.f) {
-    st = o;
-    return;
-  }
-  const float dc = o.c - st.c;
-  st.s += o.s + dc * o.l;
-  st.l += o.l;
-#pragma unroll
-  for (int c = 0; c < N; ++c) {
-    st.a1[c] += o.a1[c] + dc * o.a2[c];
-    st.a2[c] += o.a2[c];
-  }
-}
 
 // dQ and the row statistics of one row from its state (all lanes of the
 // row's group; lane gl holds channels [gl*N, gl*N + N)).
@@ -343,19 +505,19 @@ __global__ __launch_bounds__(BLOCK) void k_bwd_rows(BwdArgs a) {
   for (int c = 0; c < N; ++c) q[c] *= a.qscale;
   const float lse2 = a.lse[row * H + h] * LOG2E;
   RowState<N> st;
-  st.s = st.l = st.c = 0.f;
-#pragma unroll
-  for (int c = 0; c < N; ++c) st.a1[c] = st.a2[c] = 0.f;
-  const int gstart = wk.wave_item ? grp : 0, gstep = wk.wave_item ? RPW : 1;
+  st.init();
+  const int gstep = wk.wave_item ? RPW : 1;
+  int64_t e = (int64_t)wk.eb + (wk.wave_item ? grp : 0);
+  int32_t jn[U];
+  if (e < wk.ee) round_ids<U>(a.idx, e, wk.ee, gstep, jn);
   bool first = true;
-  for (int64_t e = (int64_t)wk.eb + gstart; e < wk.ee; e += (int64_t)gstep * U) {
+  for (; e < wk.ee; e += (int64_t)gstep * U) {
     int32_t j[U];
     bool ok[U];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      const int64_t eu = e + (int64_t)u * gstep;
-      ok[u] = eu < wk.ee;
-      j[u] = a.idx[ok[u] ? eu : e];
+      j[u] = jn[u];
+      ok[u] = e + (int64_t)u * gstep < wk.ee;
     }
     typename Raw<T>::type kr[U], vr[U];
 #pragma unroll
@@ -370,6 +532,8 @@ __global__ __launch_bounds__(BLOCK) void k_bwd_rows(BwdArgs a) {
         b[u] = a.bias[(ok[u] ? eu : e) * H + h] * LOG2E;
       }
     }
+    const int64_t en = e + (int64_t)gstep * U;
+    if (en < wk.ee) round_ids<U>(a.idx, en, wk.ee, gstep, jn);
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       float kx[N], vx[N];
@@ -398,72 +562,43 @@ __global__ __launch_bounds__(BLOCK) void k_bwd_rows(BwdArgs a) {
     first = false;
   }
   if (wk.wave_item) {
-#pragma unroll
-    for (int off = G; off < WAVE; off <<= 1) {
-      RowState<N> o;
-      o.s = __shfl_xor(st.s, off);
-      o.l = __shfl_xor(st.l, off);
-      o.c = __shfl_xor(st.c, off);
-#pragma unroll
-      for (int c = 0; c < N; ++c) {
-        o.a1[c] = __shfl_xor(st.a1[c], off);
-        o.a2[c] = __shfl_xor(st.a2[c], off);
-      }
-      row_merge(st, o);
-    }
+    wave_combine<RowState<N>, G>(st);
     if (grp != 0) return;
     if (wk.slot >= 0) {
-      float *pa = a.part_rows + (int64_t)wk.slot * (2 * D + 3 * H);
-#pragma unroll
-      for (int c = 0; c < N; ++c) {
-        pa[gl * N + c] = st.a1[c];
-        pa[D + gl * N + c] = st.a2[c];
-      }
-      if (gl % HL == 0) {
-        pa[2 * D + h] = st.s;
-        pa[2 * D + H + h] = st.l;
-        pa[2 * D + 2 * H + h] = st.c;
-      }
+      st.template put<D, H>(a.part_rows + (int64_t)wk.slot * rows_slot_floats(D, H), gl, h,
+                            gl % HL == 0);
       return;
     }
   }
   finish_row<T, HL, H>(a, row, gl, h, lse2, st);
 }
 
-// Split rows: combine the pieces' states in piece order, then dQ and the row
-// statistics.
 template <typename T, int HL, int H>
 __global__ __launch_bounds__(BLOCK) void k_bwd_rows_merge(BwdArgs a) {
   constexpr int N = Vec<T>::N, G = HL * H, D = G * N;
-  const int64_t w = (int64_t)blockIdx.x * WPB + threadIdx.x / WAVE;
-  const int lane = threadIdx.x & (WAVE - 1);
-  if (w >= a.rows.n_merges || lane >= G) return;
-  const int gl = lane, h = gl / HL;
-  const int32_t *rec = a.rows.merges + 3 * w;
+  const int lane = threadIdx.x & (WAVE - 1), grp = lane / G, gl = lane % G, h = gl / HL;
+  const int32_t *rec = a.rows.merges + 3 * (int64_t)blockIdx.x;
   const int64_t row = rec[0], first = rec[1], nch = rec[2];
   RowState<N> st;
-  st.s = st.l = st.c = 0.f;
-#pragma unroll
-  for (int c = 0; c < N; ++c) st.a1[c] = st.a2[c] = 0.f;
-  for (int64_t k = 0; k < nch; ++k) {
-    const float *pa = a.part_rows + (first + k) * (2 * D + 3 * H);
-    RowState<N> o;
-#pragma unroll
-    for (int c = 0; c < N; ++c) {
-      o.a1[c] = pa[gl * N + c];
-      o.a2[c] = pa[D + gl * N + c];
-    }
-    o.s = pa[2 * D + h];
-    o.l = pa[2 * D + H + h];
-    o.c = pa[2 * D + 2 * H + h];
-    row_merge(st, o);
-  }
-  finish_row<T, HL, H>(a, row, gl, h, a.lse[row * H + h] * LOG2E, st);
+  if (merge_pieces<RowState<N>, D, H, G, rows_slot_floats(D, H)>(st, a.part_rows, first, nch,
+                                                                 threadIdx.x / WAVE, grp, gl, h))
+    finish_row<T, HL, H>(a, row, gl, h, a.lse[row * H + h] * LOG2E, st);
 }
 
 // ---------------------------------------------------------------------------
-// backward, column pass over A^T: dK, dV
+// backward, column pass over A^T: dK, dV and dbias
 // ---------------------------------------------------------------------------
+template <typename T, int HL, int H>
+__device__ inline void finish_col(const BwdArgs &a, int64_t col, int gl,
+                                  const ColState<Vec<T>::N> &st) {
+  constexpr int N = Vec<T>::N, D = HL * H * N;
+  float k[N];
+#pragma unroll
+  for (int c = 0; c < N; ++c) k[c] = st.k[c] * a.scale;
+  Vec<T>::store((T *)a.dK + col * D + gl * N, k);
+  Vec<T>::store((T *)a.dV + col * D + gl * N, st.v);
+}
+
 template <typename T, int HL, int H, int U, bool BIAS>
 __global__ __launch_bounds__(BLOCK) void k_bwd_cols(BwdArgs a) {
   constexpr int N = Vec<T>::N, G = HL * H, D = G * N, RPW = WAVE / G;
@@ -475,18 +610,23 @@ __global__ __launch_bounds__(BLOCK) void k_bwd_cols(BwdArgs a) {
   float k[N], v[N];
   Vec<T>::load((const T *)a.K + col * D + gl * N, k);
   Vec<T>::load((const T *)a.V + col * D + gl * N, v);
-  float ak[N], av[N];
-#pragma unroll
-  for (int c = 0; c < N; ++c) ak[c] = av[c] = 0.f;
-  const int gstart = wk.wave_item ? grp : 0, gstep = wk.wave_item ? RPW : 1;
-  for (int64_t t = (int64_t)wk.eb + gstart; t < wk.ee; t += (int64_t)gstep * U) {
-    int32_t i[U];
+  ColState<N> st;
+  st.init();
+  const int gstep = wk.wave_item ? RPW : 1;
+  int64_t t = (int64_t)wk.eb + (wk.wave_item ? grp : 0);
+  int32_t in_[U], pn[U];
+  if (t < wk.ee) {
+    round_ids<U>(a.idx_t, t, wk.ee, gstep, in_);
+    if constexpr (BIAS) round_ids<U>(a.perm, t, wk.ee, gstep, pn);
+  }
+  for (; t < wk.ee; t += (int64_t)gstep * U) {
+    int32_t i[U], eid[U];
     bool ok[U];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      const int64_t tu = t + (int64_t)u * gstep;
-      ok[u] = tu < wk.ee;
-      i[u] = a.idx_t[ok[u] ? tu : t];
+      i[u] = in_[u];
+      if constexpr (BIAS) eid[u] = pn[u];
+      ok[u] = t + (int64_t)u * gstep < wk.ee;
     }
     typename Raw<T>::type qr[U], gr[U];
     float2 rs[U];
@@ -497,14 +637,14 @@ __global__ __launch_bounds__(BLOCK) void k_bwd_cols(BwdArgs a) {
 #pragma unroll
     for (int u = 0; u < U; ++u) rs[u] = a.rowstat[(int64_t)i[u] * H + h];
     float b[U];
-    int64_t eid[U];
     if constexpr (BIAS) {
 #pragma unroll
-      for (int u = 0; u < U; ++u) {
-        const int64_t tu = t + (int64_t)u * gstep;
-        eid[u] = a.perm[ok[u] ? tu : t];
-        b[u] = a.bias[eid[u] * H + h] * LOG2E;
-      }
+      for (int u = 0; u < U; ++u) b[u] = a.bias[(int64_t)eid[u] * H + h] * LOG2E;
+    }
+    const int64_t tn = t + (int64_t)gstep * U;
+    if (tn < wk.ee) {
+      round_ids<U>(a.idx_t, tn, wk.ee, gstep, in_);
+      if constexpr (BIAS) round_ids<U>(a.perm, tn, wk.ee, gstep, pn);
     }
 #pragma unroll
     for (int u = 0; u < U; ++u) {
@@ -525,66 +665,35 @@ __global__ __launch_bounds__(BLOCK) void k_bwd_cols(BwdArgs a) {
       const float ds = p * (du - rs[u].y);
 #pragma unroll
       for (int c = 0; c < N; ++c) {
-        av[c] = fmaf(p, gx[c], av[c]);
-        ak[c] = fmaf(ds, qx[c], ak[c]);
+        st.v[c] = fmaf(p, gx[c], st.v[c]);
+        st.k[c] = fmaf(ds, qx[c], st.k[c]);
       }
       if constexpr (BIAS) {
-        if (ok[u] && gl % HL == 0) a.dbias[eid[u] * H + h] = ds;
+        if (ok[u] && gl % HL == 0) a.dbias[(int64_t)eid[u] * H + h] = ds;
       }
     }
   }
   if (wk.wave_item) {
-#pragma unroll
-    for (int off = G; off < WAVE; off <<= 1) {
-#pragma unroll
-      for (int c = 0; c < N; ++c) {
-        ak[c] += __shfl_xor(ak[c], off);
-        av[c] += __shfl_xor(av[c], off);
-      }
-    }
+    wave_combine<ColState<N>, G>(st);
     if (grp != 0) return;
     if (wk.slot >= 0) {
-      float *pk = a.part_cols + (int64_t)wk.slot * 2 * D + gl * N;
-      float *pv = pk + D;
-#pragma unroll
-      for (int c = 0; c < N; c += 4) {
-        *reinterpret_cast<float4 *>(pk + c) = make_float4(ak[c], ak[c + 1], ak[c + 2], ak[c + 3]);
-        *reinterpret_cast<float4 *>(pv + c) = make_float4(av[c], av[c + 1], av[c + 2], av[c + 3]);
-      }
+      st.template put<D, H>(a.part_cols + (int64_t)wk.slot * cols_slot_floats(D, H), gl, h, false);
       return;
     }
   }
-#pragma unroll
-  for (int c = 0; c < N; ++c) ak[c] *= a.scale;
-  Vec<T>::store((T *)a.dK + col * D + gl * N, ak);
-  Vec<T>::store((T *)a.dV + col * D + gl * N, av);
+  finish_col<T, HL, H>(a, col, gl, st);
 }
 
-// Split columns: sum the pieces' dK, dV partials in piece order.
 template <typename T, int HL, int H>
 __global__ __launch_bounds__(BLOCK) void k_bwd_cols_merge(BwdArgs a) {
   constexpr int N = Vec<T>::N, G = HL * H, D = G * N;
-  const int64_t w = (int64_t)blockIdx.x * WPB + threadIdx.x / WAVE;
-  const int lane = threadIdx.x & (WAVE - 1);
-  if (w >= a.cols.n_merges || lane >= G) return;
-  const int gl = lane;
-  const int32_t *rec = a.cols.merges + 3 * w;
-  const int64_t seg = rec[0], first = rec[1], nch = rec[2];
-  float x[N], z[N];
-#pragma unroll
-  for (int c = 0; c < N; ++c) x[c] = z[c] = 0.f;
-  for (int64_t k = 0; k < nch; ++k) {
-    const float *pk = a.part_cols + (first + k) * 2 * D + gl * N, *pv = pk + D;
-#pragma unroll
-    for (int c = 0; c < N; ++c) {
-      x[c] += pk[c];
-      z[c] += pv[c];
-    }
-  }
-#pragma unroll
-  for (int c = 0; c < N; ++c) x[c] *= a.scale;
-  Vec<T>::store((T *)a.dK + seg * D + gl * N, x);
-  Vec<T>::store((T *)a.dV + seg * D + gl * N, z);
+  const int lane = threadIdx.x & (WAVE - 1), grp = lane / G, gl = lane % G, h = gl / HL;
+  const int32_t *rec = a.cols.merges + 3 * (int64_t)blockIdx.x;
+  const int64_t col = rec[0], first = rec[1], nch = rec[2];
+  ColState<N> st;
+  if (merge_pieces<ColState<N>, D, H, G, cols_slot_floats(D, H)>(st, a.part_cols, first, nch,
+                                                                 threadIdx.x / WAVE, grp, gl, h))
+    finish_col<T, HL, H>(a, col, gl, st);
 }
 
 // ---------------------------------------------------------------------------
@@ -610,7 +719,7 @@ static gt_status run_fwd(const FwdArgs &a, bool bias, hipStream_t st) {
   }
   if (a.s.n_merges > 0) {
     const int tok = prof_begin(PK_FWD_MERGE, st);
-    k_fwd_merge<T, HL, H><<<dim3((unsigned)cdiv(a.s.n_merges, WPB)), BLOCK, 0, st>>>(a);
+    k_fwd_merge<T, HL, H><<<dim3((unsigned)a.s.n_merges), BLOCK, 0, st>>>(a);
     prof_end(tok, st);
     GT_CHECK_LAUNCH();
   }
@@ -631,7 +740,7 @@ static gt_status run_bwd(const BwdArgs &a, bool bias, hipStream_t st) {
   }
   if (a.rows.n_merges > 0) {
     const int tok = prof_begin(PK_BWD_ROWS_MERGE, st);
-    k_bwd_rows_merge<T, HL, H><<<dim3((unsigned)cdiv(a.rows.n_merges, WPB)), BLOCK, 0, st>>>(a);
+    k_bwd_rows_merge<T, HL, H><<<dim3((unsigned)a.rows.n_merges), BLOCK, 0, st>>>(a);
     prof_end(tok, st);
     GT_CHECK_LAUNCH();
   }
@@ -646,7 +755,7 @@ static gt_status run_bwd(const BwdArgs &a, bool bias, hipStream_t st) {
   }
   if (a.cols.n_merges > 0) {
     const int tok = prof_begin(PK_BWD_COLS_MERGE, st);
-    k_bwd_cols_merge<T, HL, H><<<dim3((unsigned)cdiv(a.cols.n_merges, WPB)), BLOCK, 0, st>>>(a);
+    k_bwd_cols_merge<T, HL, H><<<dim3((unsigned)a.cols.n_merges), BLOCK, 0, st>>>(a);
     prof_end(tok, st);
     GT_CHECK_LAUNCH();
   }
@@ -724,7 +833,7 @@ static Sched sched_of(const gt_sched &s, const int32_t *ptr) {
 
 gt_status launch_fwd(const gt_graph *g, int heads, int head_dim, gt_dtype dt, float scale,
                      const void *Q, const void *K, const void *V, const float *bias, void *Y,
-                     float *lse, float *part_ml, float *part_acc, hipStream_t st) {
+                     float *lse, float *part, hipStream_t st) {
   FwdArgs a;
   a.s = sched_of(g->rows, g->indptr);
   a.idx = g->indices;
@@ -734,8 +843,7 @@ gt_status launch_fwd(const gt_graph *g, int heads, int head_dim, gt_dtype dt, fl
   a.bias = bias;
   a.Y = Y;
   a.lse = lse;
-  a.part_ml = part_ml;
-  a.part_acc = part_acc;
+  a.part = part;
   a.qscale = scale * LOG2E;
   gt_status rc = GT_OK;
   FwdF f{a, bias != nullptr, st, rc};

@@ -12,7 +12,7 @@ namespace gt {
 // handled by a lane group inside a wavefront; longer ones by whole
 // wavefronts, in pieces of at most DEFAULT_CHUNK nonzeros.
 constexpr int32_t DEFAULT_T_SMALL = 32;
-constexpr int32_t DEFAULT_CHUNK = 2048;
+constexpr int32_t DEFAULT_CHUNK = 256;
 
 constexpr int SORT_TILE_ITEMS = 4096;   // items per radix-sort block
 constexpr int SCAN_TILE_ITEMS = 4096;   // items per scan block
@@ -22,6 +22,16 @@ constexpr int SCAN_TILE_ITEMS = 4096;   // items per scan block
 inline int64_t sched_cap(int64_t n_seg, int64_t nnz, int32_t chunk) {
   return n_seg + nnz / chunk + 1;
 }
+
+// Floats per piece slot of a split segment, for each pass (D = heads *
+// head_dim, H = heads; a multiple of 4 so slots stay 16-byte aligned):
+//   forward   [acc D][m H][l H]
+//   row pass  [A1 D][A2 D][S H][L H][c H]
+//   column    [dK D][dV D]
+constexpr int64_t round4(int64_t x) { return (x + 3) / 4 * 4; }
+constexpr int64_t fwd_slot_floats(int64_t D, int64_t H) { return round4(D + 2 * H); }
+constexpr int64_t rows_slot_floats(int64_t D, int64_t H) { return round4(2 * D + 3 * H); }
+constexpr int64_t cols_slot_floats(int64_t D, int64_t) { return 2 * D; }
 
 struct MetaLayout {
   size_t indptr_t, indices_t, perm;
