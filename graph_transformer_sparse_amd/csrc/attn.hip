@@ -699,7 +699,7 @@ __global__ __launch_bounds__(BLOCK) void k_bwd_cols_merge(BwdArgs a) {
 // ---------------------------------------------------------------------------
 // host side: shape dispatch and launches
 // ---------------------------------------------------------------------------
-constexpr int UNROLL = 4;
+constexpr int UNROLL = 2;   // edges per lane group per round
 
 static int64_t waves_for(const Sched &s, int rpw) {
   return s.n_items + s.n_mid + cdiv(s.n_small, rpw);

@@ -12,7 +12,7 @@ namespace gt {
 // handled by a lane group inside a wavefront; longer ones by whole
 // wavefronts, in pieces of at most DEFAULT_CHUNK nonzeros.
 constexpr int32_t DEFAULT_T_SMALL = 32;
-constexpr int32_t DEFAULT_CHUNK = 256;
+constexpr int32_t DEFAULT_CHUNK = 512;
 
 constexpr int SORT_TILE_ITEMS = 4096;   // items per radix-sort block
 constexpr int SCAN_TILE_ITEMS = 4096;   // items per scan block

@@ -230,9 +230,19 @@ static int bits_for(int64_t maxval) {
 // ---------------------------------------------------------------------------
 // transpose
 // ---------------------------------------------------------------------------
-__global__ void k_count_cols(const int32_t *indices, int64_t nnz, uint32_t *cnt) {
-  const int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (e < nnz) atomicAdd(&cnt[indices[e]], 1u);
+// indptr_t[c] = number of edges with column < c, found by binary search in
+// the column keys sorted by the radix sort (c = 0 .. n_cols).
+__global__ void k_col_ptr(const uint32_t *sorted_cols, int64_t nnz, int64_t n_cols,
+                          int32_t *indptr_t) {
+  const int64_t c = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (c > n_cols) return;
+  int64_t lo = 0, hi = nnz;  // first position with key >= c
+  while (lo < hi) {
+    const int64_t mid = (lo + hi) >> 1;
+    if ((int64_t)sorted_cols[mid] < c) lo = mid + 1;
+    else hi = mid;
+  }
+  indptr_t[c] = (int32_t)lo;
 }
 
 // Row of a CSR edge: the last r with indptr[r] <= e (indptr non-decreasing).
@@ -262,15 +272,31 @@ struct Misc {  // device counters in the meta buffer
   uint32_t csr_flags, csr_first;
 };
 
-__global__ void k_degree_stats(const int32_t *ptr, int64_t n, int32_t t_small, int32_t t_mid,
-                               Misc *m) {
+// Maximum degree and tier counts: each wavefront reduces its lanes with
+// shuffles, then one lane per wavefront updates the counters.
+__global__ __launch_bounds__(256) void k_degree_stats(const int32_t *ptr, int64_t n,
+                                                      int32_t t_small, int32_t t_mid, Misc *m) {
   const int64_t s = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (s >= n) return;
-  const int32_t d = ptr[s + 1] - ptr[s];
-  atomicMax(&m->max_degree, (uint32_t)d);
-  if (d > t_mid) atomicAdd(&m->n_big, 1u);
-  else if (d > t_small) atomicAdd(&m->n_mid, 1u);
-  else atomicAdd(&m->n_small, 1u);
+  uint32_t d = 0, big = 0, mid = 0, small = 0;
+  if (s < n) {
+    d = (uint32_t)(ptr[s + 1] - ptr[s]);
+    big = (int32_t)d > t_mid;
+    mid = !big && (int32_t)d > t_small;
+    small = !big && !mid;
+  }
+#pragma unroll
+  for (int o = WAVE / 2; o > 0; o >>= 1) {
+    d = max(d, (uint32_t)__shfl_xor((int)d, o));
+    big += __shfl_xor((int)big, o);
+    mid += __shfl_xor((int)mid, o);
+    small += __shfl_xor((int)small, o);
+  }
+  if ((threadIdx.x & (WAVE - 1)) == 0) {
+    atomicMax(&m->max_degree, d);
+    if (big) atomicAdd(&m->n_big, big);
+    if (mid) atomicAdd(&m->n_mid, mid);
+    if (small) atomicAdd(&m->n_small, small);
+  }
 }
 
 __global__ void k_degree_keys(const int32_t *ptr, int64_t n, uint32_t maxd, uint32_t *key) {
@@ -449,20 +475,14 @@ extern "C" gt_status gt_graph_prepare(const int32_t *indptr, const int32_t *indi
   Misc *misc = (Misc *)at(L.misc);
   const int TB = 256;
 
-  // CSR^T row pointer: column counts, then their exclusive scan (in place).
-  uint32_t *cnt = (uint32_t *)g.indptr_t;
-  GT_HIP(hipMemsetAsync(cnt, 0, sizeof(uint32_t) * (size_t)(n_cols + 1), s));
-  if (nnz > 0) {
-    k_count_cols<<<dim3((unsigned)cdiv(nnz, TB)), dim3(TB), 0, s>>>(indices, nnz, cnt);
-    GT_CHECK_LAUNCH();
-  }
-  gt_status st = excl_scan(cnt, cnt, n_cols + 1, b.bsum, nullptr, s);
-  if (st != GT_OK) return st;
-  // perm: edge ids stably sorted by column; indices_t: their source rows
+  // perm: edge ids stably sorted by column; indptr_t: where each column's
+  // run starts in the sorted keys; indices_t: the source rows of perm
   uint32_t *ks, *vs;
-  st = radix_sort((const uint32_t *)indices, nullptr, nnz, bits_for(n_cols - 1), b, s,
-                  &ks, &vs);
+  gt_status st = radix_sort((const uint32_t *)indices, nullptr, nnz, bits_for(n_cols - 1), b, s,
+                            &ks, &vs);
   if (st != GT_OK) return st;
+  k_col_ptr<<<dim3((unsigned)cdiv(n_cols + 1, TB)), dim3(TB), 0, s>>>(ks, nnz, n_cols, g.indptr_t);
+  GT_CHECK_LAUNCH();
   if (nnz > 0) {
     GT_HIP(hipMemcpyAsync(g.perm, vs, sizeof(int32_t) * (size_t)nnz, hipMemcpyDeviceToDevice, s));
     k_source_rows<<<dim3((unsigned)cdiv(nnz, TB)), dim3(TB), 0, s>>>(indptr, n_rows, g.perm, nnz,

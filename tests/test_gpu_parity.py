@@ -121,3 +121,29 @@ def test_autograd_function_matches_abi():
     assert torch.equal(y.detach(), ref[0])
     assert torch.equal(q.grad, ref[2]) and torch.equal(k.grad, ref[3])
     assert torch.equal(v.grad, ref[4]) and torch.equal(b.grad, ref[5])
+
+
+@pytest.mark.parametrize("case", ["no_edges", "all_rows_empty_but_one", "no_columns"])
+def test_degenerate_graphs(case):
+    """Edge cases of the method: no edges at all (Y = 0, lse = -inf, all
+    gradients 0), a single edge in a large graph, and a graph whose
+    key/value side is empty (M = 0, so K, V, dK, dV have no rows)."""
+    if case == "no_edges":
+        R, M = 50, 40
+        ip, ix = np.zeros(R + 1, np.int32), np.zeros(0, np.int32)
+    elif case == "all_rows_empty_but_one":
+        R, M = 300, 700
+        ip, ix = I.csr_from_rows([[]] * 299 + [[123]], M)
+    else:
+        R, M = 20, 0
+        ip, ix = np.zeros(R + 1, np.int32), np.zeros(0, np.int32)
+    for dt, H, dh in (("f32", 2, 32), ("bf16", 4, 16)):
+        P = I.small_problem(77, ip, ix, M, H, dh, dt, bias=(case != "no_columns"))
+        out = run_gpu(P, (2, 4, 4))
+        Y, lse, dQ, dK, dV, dB = out
+        if case != "all_rows_empty_but_one":
+            assert torch.all(Y == 0) and torch.all(dQ == 0)
+            assert torch.all(torch.isneginf(lse))
+            assert dK.numel() == M * H * dh and torch.all(dK == 0) and torch.all(dV == 0)
+        else:
+            check_full(P, out)
