@@ -42,7 +42,7 @@ void clear_error() { g_err[0] = 0; }
 namespace {
 struct Prof {
   std::mutex mu;
-  bool on = false;
+  int32_t mask = 0;                                     // kernels being timed
   std::vector<std::pair<hipEvent_t, hipEvent_t>> pool;  // reusable event pairs
   std::vector<int> kind;                                // kernel of pool[i] in use
   size_t used = 0;
@@ -58,7 +58,7 @@ const char *const kPkNames[PK_COUNT] = {"fwd",      "fwd_merge",      "bwd_rows"
 int prof_begin(ProfKernel k, hipStream_t s) {
   Prof &p = prof();
   std::lock_guard<std::mutex> lk(p.mu);
-  if (!p.on) return -1;
+  if (!(p.mask & (1 << k))) return -1;
   if (p.used == p.pool.size()) {
     hipEvent_t a, b;
     if (hipEventCreate(&a) != hipSuccess) return -1;
@@ -202,10 +202,10 @@ extern "C" gt_status gt_attn_bwd(const gt_graph *g, int32_t heads, int32_t head_
                     (float *)(wb + w.part_cols), (hipStream_t)stream);
 }
 
-extern "C" gt_status gt_prof_enable(int32_t on) {
+extern "C" gt_status gt_prof_enable(int32_t kernel_mask) {
   Prof &p = prof();
   std::lock_guard<std::mutex> lk(p.mu);
-  p.on = on != 0;
+  p.mask = kernel_mask & ((1 << PK_COUNT) - 1);
   return GT_OK;
 }
 

@@ -255,8 +255,19 @@ def gt_attn_bwd(g: Graph, Q, K, V, lse, dY, bias=None, scale=None, work=None,
     return dQ, dK, dV, dbias
 
 
-def prof_enable(on: bool = True):
-    _check(lib().gt_prof_enable(1 if on else 0), "gt_prof_enable")
+PROF_KERNELS = ["fwd", "fwd_merge", "bwd_rows", "bwd_rows_merge", "bwd_cols", "bwd_cols_merge"]
+
+
+def prof_enable(kernels=True):
+    """Time the launches of ``kernels`` (a list of names; True: all; False:
+    none) with HIP events."""
+    if kernels is True:
+        mask = (1 << len(PROF_KERNELS)) - 1
+    elif not kernels:
+        mask = 0
+    else:
+        mask = sum(1 << PROF_KERNELS.index(k) for k in kernels)
+    _check(lib().gt_prof_enable(mask), "gt_prof_enable")
 
 
 def prof_reset():

@@ -187,11 +187,14 @@ gt_status gt_attn_bwd(const gt_graph *g, int32_t heads, int32_t head_dim, gt_dty
 
 /* ---- instrumentation and misc ----------------------------------------- */
 
-/* When enabled, every kernel launch is bracketed by HIP events on its own
- * stream, and gt_prof_query returns the summed device time and the launch
- * count per kernel name ("fwd", "fwd_merge", "bwd_rows", "bwd_rows_merge",
- * "bwd_cols", "bwd_cols_merge").  gt_prof_query synchronises the events. */
-gt_status gt_prof_enable(int32_t on);
+/* Kernel timing.  Bit k of kernel_mask selects kernel k of "fwd",
+ * "fwd_merge", "bwd_rows", "bwd_rows_merge", "bwd_cols", "bwd_cols_merge"
+ * (0: timing off, GT_PROF_ALL: all); every launch of a selected kernel is
+ * bracketed by HIP events on its own stream, and gt_prof_query returns the
+ * summed device time and the launch count per kernel name since the last
+ * gt_prof_reset.  gt_prof_query synchronises the events. */
+#define GT_PROF_ALL 0x3f
+gt_status gt_prof_enable(int32_t kernel_mask);
 gt_status gt_prof_reset(void);
 gt_status gt_prof_query(const char *kernel, double *total_ms, int64_t *launches);
 
