@@ -28,6 +28,7 @@ import numpy as np
 
 # stream ids of the seeded generators
 S_GRAPH, S_Q, S_K, S_V, S_DY, S_BIAS = 0, 1, 2, 3, 4, 5
+S_X, S_WQ, S_WK, S_WV, S_WO, S_DZ = 6, 7, 8, 9, 10, 11
 
 
 @dataclass(frozen=True)
@@ -387,3 +388,20 @@ def random_graph(seed: int, n_rows: int, n_cols: int, degrees, self_loops: bool 
             cols = rng.choice(n_cols, size=d, replace=False)
         rows.append(cols)
     return csr_from_rows(rows, n_cols)
+
+
+# ----------------------------------------------------------------------------
+# inputs of a whole layer (node features, projection weights, output gradient)
+# ----------------------------------------------------------------------------
+
+def layer_inputs(cfg_idx: int, n: int, d: int, dtype: str):
+    """X [n, d] and dZ [n, d] ~ N(0, 1); weights W_q, W_k, W_v, W_o [d, d]
+    ~ N(0, 1/d) (so a projection of unit-variance features has unit
+    variance).  float32 arrays holding exactly the values of ``dtype``."""
+    def draw(stream, shape, std):
+        x = rng_for(cfg_idx, stream).normal(0.0, std, shape).astype(np.float32)
+        return to_bf16_values(x) if dtype == "bf16" else x
+    X = draw(S_X, (n, d), 1.0)
+    W = {k: draw(s, (d, d), d ** -0.5) for k, s in (("q", S_WQ), ("k", S_WK), ("v", S_WV), ("o", S_WO))}
+    dZ = draw(S_DZ, (n, d), 1.0)
+    return X, W, dZ
