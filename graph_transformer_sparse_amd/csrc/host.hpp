@@ -5,6 +5,7 @@
 #include <stdint.h>
 
 #include "../../include/gt_attn.h"
+#include "../../include/gt_proj.h"
 
 namespace gt {
 

@@ -19,7 +19,7 @@ import torch
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "_build", "libgtattn.so")
-HEADER = os.path.join(os.path.dirname(HERE), "include", "gt_attn.h")
+INCLUDE = os.path.join(os.path.dirname(HERE), "include")
 
 GT_OK = 0
 GT_F32, GT_BF16 = 0, 1
@@ -55,10 +55,13 @@ _lib = None
 
 
 def header_functions() -> list[str]:
-    """Names of the functions include/gt_attn.h declares."""
-    text = open(HEADER).read()
-    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(gt_[a-z0-9_]+)\s*\(", text)))
+    """Names of the functions the headers in include/ declare."""
+    names = set()
+    for f in sorted(os.listdir(INCLUDE)):
+        if f.endswith(".h"):
+            text = re.sub(r"/\*.*?\*/", "", open(os.path.join(INCLUDE, f)).read(), flags=re.S)
+            names.update(re.findall(r"\b(gt_[a-z0-9_]+)\s*\(", text))
+    return sorted(names)
 
 
 def lib():
@@ -304,3 +307,110 @@ class GTAttnFn(torch.autograd.Function):
 
 def sparse_graph_attention(g: Graph, Q, K, V, bias=None, scale=None):
     return GTAttnFn.apply(g, Q, K, V, bias, scale)
+
+
+# ----------------------------------------------------------------------------
+# dense parts of the layer (include/gt_proj.h)
+# ----------------------------------------------------------------------------
+
+def _proj_lib():
+    L = lib()
+    if not getattr(L, "_proj_sigs", False):
+        sig = {
+            "gt_proj_qkv": (_i32, [_i64, _i32, _i32] + [_P] * 8),
+            "gt_proj_out": (_i32, [_i64, _i32, _i32] + [_P] * 5),
+            "gt_proj_bwd_data": (_i32, [_i64, _i32, _i32] + [_P] * 10),
+            "gt_proj_work_bytes": (_sz, [_i64, _i32]),
+            "gt_proj_bwd_weight": (_i32, [_i64, _i32, _i32] + [_P] * 10 + [_sz, _P]),
+        }
+        for name, (res, args) in sig.items():
+            f = getattr(L, name)
+            f.restype = res
+            f.argtypes = args
+        L._proj_sigs = True
+    return L
+
+
+def _nd(X):
+    assert X.dim() == 2 and X.is_contiguous()
+    return X.shape[0], X.shape[1]
+
+
+def gt_proj_qkv(X, Wq, Wk, Wv):
+    """Q, K, V = X W_q, X W_k, X W_v; X [n, d], W [d, d] (f32 or bf16)."""
+    n, d = _nd(X)
+    Q, K, V = (torch.empty_like(X) for _ in range(3))
+    _check(_proj_lib().gt_proj_qkv(n, d, _dt(X.dtype), _ptr(X), _ptr(Wq), _ptr(Wk), _ptr(Wv),
+                                   _ptr(Q), _ptr(K), _ptr(V), _stream(X.device)), "gt_proj_qkv")
+    return Q, K, V
+
+
+def gt_proj_out(X, Wo, Y):
+    """Z = X W_o + Y."""
+    n, d = _nd(X)
+    Z = torch.empty_like(X)
+    _check(_proj_lib().gt_proj_out(n, d, _dt(X.dtype), _ptr(X), _ptr(Wo), _ptr(Y), _ptr(Z),
+                                   _stream(X.device)), "gt_proj_out")
+    return Z
+
+
+def gt_proj_bwd_data(dZ, dQ, dK, dV, Wo, Wq, Wk, Wv):
+    """dX = dZ W_o^T + dQ W_q^T + dK W_k^T + dV W_v^T."""
+    n, d = _nd(dZ)
+    dX = torch.empty_like(dZ)
+    _check(_proj_lib().gt_proj_bwd_data(n, d, _dt(dZ.dtype), _ptr(dZ), _ptr(dQ), _ptr(dK),
+                                        _ptr(dV), _ptr(Wo), _ptr(Wq), _ptr(Wk), _ptr(Wv),
+                                        _ptr(dX), _stream(dZ.device)), "gt_proj_bwd_data")
+    return dX
+
+
+def gt_proj_bwd_weight(X, dZ, dQ, dK, dV, work=None):
+    """dW_o, dW_q, dW_k, dW_v = X^T dZ, X^T dQ, X^T dK, X^T dV (float32)."""
+    n, d = _nd(X)
+    L = _proj_lib()
+    nb = L.gt_proj_work_bytes(n, d)
+    if work is None or work.numel() < nb:
+        work = torch.empty(nb, dtype=torch.uint8, device=X.device)
+    dW = [torch.empty((d, d), dtype=torch.float32, device=X.device) for _ in range(4)]
+    _check(L.gt_proj_bwd_weight(n, d, _dt(X.dtype), _ptr(X), _ptr(dZ), _ptr(dQ), _ptr(dK),
+                                _ptr(dV), *(_ptr(w) for w in dW), _ptr(work), work.numel(),
+                                _stream(X.device)), "gt_proj_bwd_weight")
+    return tuple(dW)
+
+
+class SGALayerFn(torch.autograd.Function):
+    """One sparse graph attention layer: Z = X W_o + attention(X W_q, X W_k,
+    X W_v) over a prepared graph, with its backward through the C ABI."""
+
+    @staticmethod
+    def forward(ctx, g: Graph, heads: int, X, Wq, Wk, Wv, Wo, bias=None, scale=None):
+        X = X.contiguous()
+        n, d = X.shape
+        Q, K, V = gt_proj_qkv(X, Wq, Wk, Wv)
+        shp = (n, heads, d // heads)
+        Y, lse = gt_attn_fwd(g, Q.view(shp), K.view(shp), V.view(shp), bias, scale)
+        Z = gt_proj_out(X, Wo, Y.view(n, d))
+        ctx.g, ctx.heads, ctx.scale, ctx.has_bias = g, heads, scale, bias is not None
+        ctx.save_for_backward(X, Wq, Wk, Wv, Wo, Q, K, V, lse,
+                              bias if bias is not None else torch.empty(0))
+        return Z
+
+    @staticmethod
+    def backward(ctx, dZ):
+        X, Wq, Wk, Wv, Wo, Q, K, V, lse, bias = ctx.saved_tensors
+        bias = bias if ctx.has_bias else None
+        dZ = dZ.contiguous()
+        n, d = X.shape
+        shp = (n, ctx.heads, d // ctx.heads)
+        dQ, dK, dV, db = gt_attn_bwd(ctx.g, Q.view(shp), K.view(shp), V.view(shp), lse,
+                                     dZ.view(shp), bias, ctx.scale)
+        dQ, dK, dV = (t.view(n, d) for t in (dQ, dK, dV))
+        dX = gt_proj_bwd_data(dZ, dQ, dK, dV, Wo, Wq, Wk, Wv)
+        dWo, dWq, dWk, dWv = gt_proj_bwd_weight(X, dZ, dQ, dK, dV)
+        cast = lambda w, ref: w.to(ref.dtype)
+        return (None, None, dX, cast(dWq, Wq), cast(dWk, Wk), cast(dWv, Wv), cast(dWo, Wo),
+                db, None)
+
+
+def sga_layer(g: Graph, heads: int, X, Wq, Wk, Wv, Wo, bias=None, scale=None):
+    return SGALayerFn.apply(g, heads, X, Wq, Wk, Wv, Wo, bias, scale)

@@ -15,6 +15,10 @@ and its gradients, given dZ:
 Readings: weights are [d, d] row-major and act as X W (the projection maps
 node features of width d to the H * dh channels of the heads, here d = H dh);
 the layer is square (every node is both a query and a key/value node).
+With ``store="bf16"`` the tensors a bf16 layer keeps in memory between its
+steps -- Q, K, V and Y in the forward, dQ, dK and dV in the backward -- are
+rounded to bf16 (nearest, ties to even) where they are stored; everything
+else stays float64.
 numpy's float64 matmul is the one library step; nothing else is fused.
 """
 from __future__ import annotations
@@ -26,6 +30,19 @@ from . import oracle as O
 
 def _f64(x):
     return np.asarray(x, dtype=np.float64)
+
+
+def round_bf16(x):
+    """Round to the nearest bfloat16 value, ties to even (finite inputs):
+    round to float32 first, then keep the top 16 bits of the float32 pattern
+    after adding half an ulp of bf16 (plus one if the kept part is odd)."""
+    u = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32).astype(np.uint64)
+    u = (u + 0x7FFF + ((u >> 16) & 1)) >> 16
+    return (u.astype(np.uint32) << 16).view(np.float32).astype(np.float64).reshape(np.shape(x))
+
+
+def _store(x, store):
+    return round_bf16(x) if store == "bf16" else x
 
 
 def proj_qkv(X, Wq, Wk, Wv):
@@ -47,27 +64,28 @@ def proj_bwd_weight(X, dZ, dQ, dK, dV):
     return Xt @ _f64(dZ), Xt @ _f64(dQ), Xt @ _f64(dK), Xt @ _f64(dV)
 
 
-def layer_fwd(indptr, indices, X, W, heads, bias=None, scale=None):
+def layer_fwd(indptr, indices, X, W, heads, bias=None, scale=None, store=None):
     """W = dict(q, k, v, o) of [d, d].  Returns dict(Q, K, V, Y, lse, Z)."""
     X = _f64(X)
     n, d = X.shape
     dh = d // heads
-    Q, K, V = proj_qkv(X, W["q"], W["k"], W["v"])
+    Q, K, V = (_store(t, store) for t in proj_qkv(X, W["q"], W["k"], W["v"]))
     r = lambda t: t.reshape(n, heads, dh)
     Y, lse = O.fwd(indptr, indices, n, r(Q), r(K), r(V), bias, scale)
-    Z = proj_out(X, W["o"], Y.reshape(n, d))
-    return dict(Q=Q, K=K, V=V, Y=Y.reshape(n, d), lse=lse, Z=Z)
+    Y = _store(Y.reshape(n, d), store)
+    Z = proj_out(X, W["o"], Y)
+    return dict(Q=Q, K=K, V=V, Y=Y, lse=lse, Z=Z)
 
 
-def layer_bwd(indptr, indices, X, W, heads, dZ, bias=None, scale=None):
+def layer_bwd(indptr, indices, X, W, heads, dZ, bias=None, scale=None, store=None):
     """Gradients of <Z, dZ>: dict(dX, dWq, dWk, dWv, dWo, dQ, dK, dV, dbias)."""
     X = _f64(X)
     n, d = X.shape
     dh = d // heads
-    Q, K, V = proj_qkv(X, W["q"], W["k"], W["v"])
+    Q, K, V = (_store(t, store) for t in proj_qkv(X, W["q"], W["k"], W["v"]))
     r = lambda t: t.reshape(n, heads, dh)
     dQ, dK, dV, dB = O.bwd(indptr, indices, n, r(Q), r(K), r(V), r(_f64(dZ)), bias, scale)
-    dQ, dK, dV = (t.reshape(n, d) for t in (dQ, dK, dV))
+    dQ, dK, dV = (_store(t.reshape(n, d), store) for t in (dQ, dK, dV))
     dX = proj_bwd_data(dZ, dQ, dK, dV, W["o"], W["q"], W["k"], W["v"])
     dWo, dWq, dWk, dWv = proj_bwd_weight(X, dZ, dQ, dK, dV)
     return dict(dX=dX, dWq=dWq, dWk=dWk, dWv=dWv, dWo=dWo, dQ=dQ, dK=dK, dV=dV, dbias=dB)

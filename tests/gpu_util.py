@@ -2,7 +2,8 @@
 parity comparison.
 
 Tolerance (fp32 1e-5, bf16 inputs with fp32 accumulation 2e-2, both
-relative), per tensor and head:
+relative), per tensor and head ([n, heads, head_dim] and [n, heads] arrays;
+other arrays as a whole):
   * the relative error ||got - ref||_2 / ||ref||_2 <= rtol, and
   * elementwise |got - ref| <= rtol*|ref| + rtol*rms(ref) + 8*u*mag, where
     rms is over the head's compared elements, u = 2^-24 is the unit roundoff
@@ -36,13 +37,17 @@ def to_np(t):
 U32 = 2.0 ** -24
 
 
-def assert_close(got, ref, rtol, name, mag=None):
+def assert_close(got, ref, rtol, name, mag=None, head_axis="auto"):
+    """head_axis: the axis whose entries get their own statistics (default:
+    axis 1 of a [n, heads, head_dim] array; None: the whole array)."""
     g = got if isinstance(got, np.ndarray) else to_np(got)
     ref = np.asarray(ref, np.float64)
     assert g.shape == ref.shape, (name, g.shape, ref.shape)
     if ref.size == 0:
         return
-    axes = tuple(a for a in range(ref.ndim) if a != 1) if ref.ndim >= 2 else (0,)
+    if head_axis == "auto":
+        head_axis = 1 if ref.ndim == 3 else None
+    axes = tuple(a for a in range(ref.ndim) if a != head_axis)
     rms = np.sqrt(np.mean(ref ** 2, axis=axes, keepdims=True))
     d2 = np.sqrt(np.sum((g - ref) ** 2, axis=axes))
     r2 = np.sqrt(np.sum(ref ** 2, axis=axes))

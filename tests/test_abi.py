@@ -13,7 +13,7 @@ from graph_transformer_sparse_amd import gtattn as T
 
 def _fresh():
     srcs = [os.path.join(B.CSRC, f) for f in os.listdir(B.CSRC)]
-    srcs.append(os.path.join(B.INCLUDE, "gt_attn.h"))
+    srcs += [os.path.join(B.INCLUDE, f) for f in os.listdir(B.INCLUDE)]
     return os.path.exists(B.LIB) and os.path.getmtime(B.LIB) >= max(map(os.path.getmtime, srcs))
 
 
@@ -27,6 +27,7 @@ def L():
 def test_exports_every_declared_function(L):
     names = T.header_functions()
     assert "gt_attn_fwd" in names and "gt_attn_bwd" in names and "gt_graph_prepare" in names
+    assert "gt_proj_qkv" in names and "gt_proj_bwd_weight" in names
     for n in names:
         assert hasattr(L, n), n
     assert L.gt_version() >= 100
@@ -137,3 +138,16 @@ def test_prof_query_checks(L):
     ms, n = C.c_double(), C.c_int64()
     assert L.gt_prof_query(b"nope", C.byref(ms), C.byref(n)) == 2
     assert L.gt_prof_query(b"fwd", C.byref(ms), C.byref(n)) == 0 and n.value == 0
+
+
+def test_proj_argument_checks(L):
+    T._proj_lib()
+    assert L.gt_proj_qkv(10, 96, 0, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None) == 4   # d
+    assert L.gt_proj_qkv(10, 128, 5, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None) == 3  # dtype
+    assert L.gt_proj_qkv(10, 128, 0, None, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None) == 1
+    assert L.gt_proj_out(10, 128, 1, FAKE, ODD, FAKE, FAKE, None) == 5
+    assert L.gt_proj_out(-1, 128, 1, FAKE, FAKE, FAKE, FAKE, None) == 2
+    nb = L.gt_proj_work_bytes(100000, 128)
+    assert nb >= 4 * 13 * 128 * 128 * 4          # 13 chunks of 8192 rows, 4 gradients
+    assert L.gt_proj_bwd_weight(100000, 128, 0, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
+                                FAKE, FAKE, nb - 1, None) == 7

@@ -44,7 +44,7 @@ def check_full(P, out, rtol=None):
     assert_close(dK, rK, rtol, "dK", m["dK"])
     assert_close(dV, rV, rtol, "dV", m["dV"])
     if P.bias is not None:
-        assert_close(dB, rB, rtol, "dbias")
+        assert_close(dB, rB, rtol, "dbias", head_axis=1)
     else:
         assert dB is None
 
@@ -96,7 +96,7 @@ def test_scale_other_than_default():
     rY, rl = O.fwd(ip, ix, 64, P.Q, P.K, P.V, P.bias, 0.3)
     rQ, rK, rV, rB = O.bwd(ip, ix, 64, P.Q, P.K, P.V, P.dY, P.bias, 0.3)
     for a, b, n in ((Y, rY, "Y"), (dQ, rQ, "dQ"), (dK, rK, "dK"), (dV, rV, "dV"), (dB, rB, "dB")):
-        assert_close(a, b, 1e-5, n)
+        assert_close(a, b, 1e-5, n, head_axis=1 if n == "dB" else "auto")
     assert_lse(lse, rl, 1e-5)
 
 

@@ -1,0 +1,97 @@
+"""Parity of the MFMA projection kernels (include/gt_proj.h) and of a whole
+sparse graph attention layer with the fp64 layer oracle (oracle/layer.py;
+the paper's Section 2.1, Eq. 3-5).
+
+Tolerance as for attention (gpu_util): per tensor relative L2 <= rtol and
+elementwise rtol*|r| + rtol*rms(r) + 8u*mag, mag = the sum of the absolute
+values of each output's terms (|A| |B| for a product A B).  Weight
+gradients are float32 for either input dtype and sum exact products of the
+inputs, so they are held to the float32 bound (1e-5) in both cases.
+"""
+import numpy as np
+import pytest
+import torch
+
+from graph_transformer_sparse_amd import gtattn as T
+from graph_transformer_sparse_amd import inputs as I
+from oracle import layer as L
+
+from gpu_util import RTOL, TDT, assert_close, dev, to_np
+
+pytestmark = pytest.mark.gpu
+
+
+def _abs(x):
+    return np.abs(np.asarray(x, np.float64))
+
+
+CASES = [(n, d, dt) for dt in ("f32", "bf16") for n, d in
+         ((1, 64), (100, 128), (128, 256), (1000, 64), (4097, 128), (20000, 256))]
+
+
+@pytest.mark.parametrize("case", CASES, ids=[f"n{n}-d{d}-{dt}" for n, d, dt in CASES])
+def test_projection_kernels(case):
+    n, d, dt = case
+    print(f"proj n={n} d={d} {dt}", flush=True)
+    X, W, dZ = I.layer_inputs(700 + n % 97, n, d, dt)
+    G = [I.layer_inputs(800 + k, n, d, dt)[2] for k in range(3)]    # stand-in dQ, dK, dV
+    Y = I.layer_inputs(900, n, d, dt)[2]
+    t = lambda a: dev(a, TDT[dt])
+    Xd, Wd = t(X), {k: t(v) for k, v in W.items()}
+    rt = RTOL[dt]
+    Q, K, V = T.gt_proj_qkv(Xd, Wd["q"], Wd["k"], Wd["v"])
+    rq = L.proj_qkv(X, W["q"], W["k"], W["v"])
+    for got, ref, k in zip((Q, K, V), rq, "qkv"):
+        assert_close(got, ref, rt, "XW" + k, _abs(X) @ _abs(W[k]))
+    Z = T.gt_proj_out(Xd, Wd["o"], t(Y))
+    assert_close(Z, L.proj_out(X, W["o"], Y), rt, "Z", _abs(X) @ _abs(W["o"]) + _abs(Y))
+    dX = T.gt_proj_bwd_data(t(dZ), t(G[0]), t(G[1]), t(G[2]), Wd["o"], Wd["q"], Wd["k"], Wd["v"])
+    rdx = L.proj_bwd_data(dZ, G[0], G[1], G[2], W["o"], W["q"], W["k"], W["v"])
+    mag = sum(_abs(a) @ _abs(W[k]).T for a, k in zip((dZ, *G), "oqkv"))
+    assert_close(dX, rdx, rt, "dX", mag)
+    dW = T.gt_proj_bwd_weight(Xd, t(dZ), t(G[0]), t(G[1]), t(G[2]))
+    rdw = L.proj_bwd_weight(X, dZ, G[0], G[1], G[2])
+    for got, ref, a, k in zip(dW, rdw, (dZ, *G), "oqkv"):
+        assert_close(got, ref, 1e-5, "dW" + k, _abs(X).T @ _abs(a))
+    torch.cuda.synchronize()
+
+
+def test_weight_gradient_is_deterministic():
+    n, d = 30000, 128
+    X, W, dZ = I.layer_inputs(11, n, d, "bf16")
+    t = lambda a: dev(a, torch.bfloat16)
+    a = T.gt_proj_bwd_weight(t(X), t(dZ), t(dZ), t(X), t(dZ))
+    b = T.gt_proj_bwd_weight(t(X), t(dZ), t(dZ), t(X), t(dZ))
+    for x, y in zip(a, b):
+        assert torch.equal(x, y)
+
+
+LAYER = [("f32", 2, 32, False), ("bf16", 4, 32, True), ("f32", 1, 64, True), ("bf16", 8, 32, False)]
+
+
+@pytest.mark.parametrize("case", LAYER, ids=[f"{a}-h{b}-d{c}-{'bias' if e else 'nobias'}" for a, b, c, e in LAYER])
+def test_layer(case):
+    dt, H, dh, bias = case
+    d = H * dh
+    n = 700
+    degs = np.random.default_rng(d).integers(0, 90, n)
+    ip, ix = I.random_graph(123 + d, n, n, degs)
+    X, W, dZ = I.layer_inputs(31 + d, n, d, dt)
+    b = I.edge_bias(41, ix.size, H) if bias else None
+    t = lambda a: dev(a, TDT[dt])
+    g = T.gt_graph_prepare(dev(ip), dev(ix), n, 4, 16, 16)
+    Xd = t(X).requires_grad_()
+    Wd = {k: t(v).requires_grad_() for k, v in W.items()}
+    bd = dev(b, torch.float32).requires_grad_() if bias else None
+    Z = T.sga_layer(g, H, Xd, Wd["q"], Wd["k"], Wd["v"], Wd["o"], bd)
+    Z.backward(t(dZ))
+    store = "bf16" if dt == "bf16" else None     # the intermediates the bf16 path stores
+    rf = L.layer_fwd(ip, ix, X, W, H, b, store=store)
+    rb = L.layer_bwd(ip, ix, X, W, H, dZ, b, store=store)
+    rt = RTOL[dt]
+    assert_close(Z, rf["Z"], rt, "Z")
+    assert_close(Xd.grad, rb["dX"], rt, "dX")
+    for k in "qkvo":
+        assert_close(Wd[k].grad, rb["dW" + k], rt, "dW" + k)
+    if bias:
+        assert_close(bd.grad, rb["dbias"], rt, "dbias", head_axis=1)

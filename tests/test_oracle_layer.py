@@ -93,3 +93,24 @@ def test_identity_and_zero_weights():
     Y, _ = O.fwd(ip, ix, n, X.reshape(n, H, dh), X.reshape(n, H, dh), X.reshape(n, H, dh))
     np.testing.assert_array_equal(f["Q"], X.astype(np.float64))
     np.testing.assert_array_equal(f["Z"], Y.reshape(n, d))
+
+
+def test_bf16_rounding_matches_torch():
+    """The oracle's own bf16 rounding agrees with torch's float32 -> bfloat16
+    conversion (round to nearest even), including exact ties."""
+    x = np.random.default_rng(9).standard_normal(100000) * 10.0 ** np.random.default_rng(10).integers(-8, 8, 100000)
+    ties = np.array([1 + 2.0 ** -8, 1 + 3 * 2.0 ** -8, -(1 + 2.0 ** -8), 2.0 ** -130])
+    for a in (x, ties):
+        t = torch.tensor(a.astype(np.float32)).to(torch.bfloat16).double().numpy()
+        np.testing.assert_array_equal(L.round_bf16(a), t)
+
+
+def test_store_none_is_unrounded():
+    n, H, dh = 20, 2, 8
+    ip, ix, X, W, dZ, _ = _problem(7, n, H, dh, False)
+    a = L.layer_fwd(ip, ix, X, W, H)
+    b = L.layer_fwd(ip, ix, X, W, H, store=None)
+    np.testing.assert_array_equal(a["Z"], b["Z"])
+    c = L.layer_fwd(ip, ix, X, W, H, store="bf16")
+    np.testing.assert_array_equal(c["Q"], L.round_bf16(a["Q"]))
+    assert np.max(np.abs(c["Z"] - a["Z"])) < 0.05 * np.max(np.abs(a["Z"]))
