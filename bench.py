@@ -57,7 +57,7 @@ def byte_model(cfg, R, M, E, M_nz):
 
 # the sources that decide what the kernels read and write: the kernels, their
 # device helpers and layouts, and the schedule they run over
-KERNEL_SOURCES = ["attn.hip", "device.hpp", "layout.hpp", "prep.hip"]
+KERNEL_SOURCES = ["attn.hip", "device.hpp", "layout.hpp", "prep.hip", "proj.hip"]
 
 
 def kernel_source_hash() -> str:
@@ -140,6 +140,9 @@ def main():
                     choices=["tiny", "mid", "large", "hub", "shard"])
     ap.add_argument("--cpu-budget", type=float, default=15.0,
                     help="seconds of oracle work for the CPU baseline (0: skip)")
+    ap.add_argument("--layer", action="store_true",
+                    help="time a whole layer (dense projections + attention, fwd+bwd) "
+                         "instead of the attention alone")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
                     help="only run a plain device-to-device copy of MIB MiB, 5 times "
                          "(calibrates the HBM byte counters against a known size)")
@@ -166,6 +169,8 @@ def main():
 
     T.lib()
     cfg = I.CONFIGS[args.config]
+    if args.layer:
+        return layer_bench(args, cfg)
     t0 = time.perf_counter()
     P = I.make_problem(cfg)
     gen_s = time.perf_counter() - t0
@@ -268,6 +273,152 @@ def main():
 
 def T_np(t):
     return t.cpu().numpy()
+
+
+MFMA_PEAK_TFLOPS = {"f32": 157.3, "bf16": 2500.0}
+
+
+def proj_model(n, d, s):
+    """Algorithmic bytes and flops of each projection kernel (every node
+    array read or written once, weights once, weight-gradient partials of
+    8192-row chunks written and read once)."""
+    chunks = -(-n // 8192)
+    nd = n * d * s
+    return {
+        "proj_qkv": (4 * nd + 3 * d * d * s, 3 * 2 * n * d * d),
+        "proj_out": (3 * nd + d * d * s, 2 * n * d * d),
+        "proj_bwd_data": (5 * nd + 4 * d * d * s, 4 * 2 * n * d * d),
+        "proj_bwd_weight": (5 * nd + 4 * d * d * 4 * (2 * chunks + 1), 4 * 2 * n * d * d),
+    }
+
+
+def layer_bench(args, cfg):
+    """A whole layer, fwd + bwd: Q/K/V = X W, attention, Z = X W_o + Y, and
+    every gradient.  Same JSON line; `detail` adds the projection kernels'
+    rates against their byte model and against the matrix-core peak."""
+    import torch
+
+    from graph_transformer_sparse_amd import gtattn as T
+    from graph_transformer_sparse_amd import inputs as I
+
+    if cfg.n_rows != cfg.n_cols:
+        print("--layer needs a square graph (every node a query and a key)", file=sys.stderr)
+        sys.exit(2)
+    t0 = time.perf_counter()
+    P = I.make_problem(cfg)
+    n, H, dh, E = cfg.n_rows, cfg.heads, cfg.head_dim, P.nnz
+    d = H * dh
+    X, W, dZ = I.layer_inputs(cfg.idx, n, d, cfg.dtype)
+    gen_s = time.perf_counter() - t0
+    dev = torch.device("cuda:0")
+    tdt = torch.float32 if cfg.dtype == "f32" else torch.bfloat16
+    put = lambda x, dt: torch.from_numpy(np.ascontiguousarray(x)).to(dt).to(dev).contiguous()
+    g = T.gt_graph_prepare(put(P.indptr, torch.int32), put(P.indices, torch.int32), n)
+    Xd, dZd = put(X, tdt), put(dZ, tdt)
+    Wd = {k: put(v, tdt) for k, v in W.items()}
+    bias = put(P.bias, torch.float32) if P.bias is not None else None
+    shp = (n, H, dh)
+    Y = torch.empty(shp, dtype=tdt, device=dev)
+    lse = torch.empty((n, H), dtype=torch.float32, device=dev)
+    dQ, dK, dV = (torch.empty(shp, dtype=tdt, device=dev) for _ in range(3))
+    dbias = torch.empty_like(bias) if bias is not None else None
+    work = torch.empty(T.gt_attn_work_bytes(g, H, dh), dtype=torch.uint8, device=dev)
+    pwork = torch.empty(T._proj_lib().gt_proj_work_bytes(n, d), dtype=torch.uint8, device=dev)
+    ev = {}
+
+    def timed(name, fn):
+        if name in ev:
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            out = fn()
+            b.record()
+            ev[name].append((a, b))
+            return out
+        return fn()
+
+    def step():
+        Q, K, V = timed("proj_qkv", lambda: T.gt_proj_qkv(Xd, Wd["q"], Wd["k"], Wd["v"]))
+        T.gt_attn_fwd(g, Q.view(shp), K.view(shp), V.view(shp), bias, P.scale, work, Y, lse)
+        timed("proj_out", lambda: T.gt_proj_out(Xd, Wd["o"], Y.view(n, d)))
+        T.gt_attn_bwd(g, Q.view(shp), K.view(shp), V.view(shp), lse, dZd.view(shp), bias,
+                      P.scale, work, dQ, dK, dV, dbias)
+        args4 = (dZd, dQ.view(n, d), dK.view(n, d), dV.view(n, d))
+        timed("proj_bwd_data", lambda: T.gt_proj_bwd_data(*args4, Wd["o"], Wd["q"], Wd["k"], Wd["v"]))
+        timed("proj_bwd_weight", lambda: T.gt_proj_bwd_weight(Xd, *args4, work=pwork))
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    # three profiled steps: every kernel's time
+    for k in ("proj_qkv", "proj_out", "proj_bwd_data", "proj_bwd_weight"):
+        ev[k] = []
+    T.prof_reset()
+    T.prof_enable(True)
+    for _ in range(3):
+        step()
+    torch.cuda.synchronize()
+    T.prof_enable(False)
+    kern = {}
+    for k in KERNELS:
+        tot, c = T.prof_query(k)
+        if c:
+            kern[k] = {"ms_per_launch": tot / c, "launches": c}
+    for k, lst in ev.items():
+        kern[k] = {"ms_per_launch": sum(a.elapsed_time(b) for a, b in lst) / len(lst),
+                   "launches": len(lst)}
+    ev.clear()
+    s = 4 if cfg.dtype == "f32" else 2
+    M_nz = int(np.count_nonzero(np.diff(T_np(g.indptr_t))))
+    model = byte_model(cfg, n, n, E, M_nz)
+    pm = proj_model(n, d, s)
+    for k, (byt, flops) in pm.items():
+        t = kern[k]["ms_per_launch"] * 1e-3
+        kern[k].update(model_GB=byt / 1e9, GBps=byt / t / 1e9, TFLOPs=flops / t / 1e12,
+                       mfma_frac=flops / t / 1e12 / MFMA_PEAK_TFLOPS[cfg.dtype])
+    for k in model:
+        if k in kern:
+            kern[k]["model_GB"] = model[k] / 1e9
+            kern[k]["GBps"] = model[k] / (kern[k]["ms_per_launch"] * 1e-3) / 1e9
+    dominant = max(kern, key=lambda k: kern[k]["ms_per_launch"])
+    T.prof_reset()
+    if dominant in KERNELS:
+        T.prof_enable([dominant])
+    else:
+        ev[dominant] = []
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    T.prof_enable(False)
+    if dominant in KERNELS:
+        tot, c = T.prof_query(dominant)
+        kern[dominant]["ms_per_launch"] = tot / c
+    else:
+        lst = ev[dominant]
+        kern[dominant]["ms_per_launch"] = sum(a.elapsed_time(b) for a, b in lst) / len(lst)
+    dom_bytes = model[dominant] if dominant in model else pm[dominant][0]
+    ach = dom_bytes / (kern[dominant]["ms_per_launch"] * 1e-3) / 1e9
+    ms_step = elapsed * 1e3 / args.steps
+    line = {
+        "metric": "GEdges/s sparse graph attention layer (dense projections + attention) fwd+bwd, 1 MI355X",
+        "value": E / (ms_step * 1e-3) / 1e9,
+        "unit": "GEdges/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms_step,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
+        "data": "synthetic (seeded generators standing in for the pages' graphs)",
+        "config": {"workload": f"{cfg.name} layer: {cfg.desc}", "nodes": n, "nnz": E,
+                   "heads": H, "head_dim": dh, "d": d, "storage": cfg.dtype,
+                   "bias": cfg.bias, "parallelism": "single GPU"},
+        "roofline": {"bound": "hbm", "kernel": dominant, "achieved": ach, "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": ach / HBM_PEAK_GBS,
+                     "traffic": traffic_record(dominant, cfg.name)},
+        "cpu_baseline": None,
+        "detail": {"kernels": kern, "input_gen_s": gen_s,
+                   "kernel_source_hash": kernel_source_hash()},
+    }
+    print(json.dumps(line), flush=True)
 
 
 if __name__ == "__main__":

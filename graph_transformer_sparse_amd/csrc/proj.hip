@@ -4,16 +4,24 @@
 // dX = dZ W_o^T + dQ W_Q^T + dK W_K^T + dV W_V^T, dW_* = X^T d*.
 //
 // These are real dense contractions, so they run on the matrix cores:
-// v_mfma_f32_32x32x8_bf16 (bf16 inputs) and v_mfma_f32_32x32x2_f32 (fp32),
+// v_mfma_f32_32x32x16_bf16 (bf16 inputs) and v_mfma_f32_32x32x2_f32 (fp32),
 // fp32 accumulation.  With n nodes >> d (d = heads * head_dim <= 256) every
-// product moves O(n d) bytes for O(n d^2) flops, so the kernels are built to
-// stream the node-feature arrays once: 128-row tiles of the [n, d] operands,
-// the [d, d] weights (L2-resident) staged through LDS in 32-wide k chunks.
+// product streams O(n d) bytes of node features for O(n d^2) flops.
 //
-// MFMA 32x32 operand layout (per lane l of the wavefront): A[m][k] with
-// m = l % 32 and k = KW*(l / 32) + i, B[k][n] with n = l % 32 and the same k,
-// i < KW (KW = 4 for bf16, 1 for fp32); accumulator element v of lane l is
-// D[m][n] with n = l % 32 and m = 8*(v / 4) + 4*(l / 32) + v % 4.
+// Operand layout.  A 16-byte "vector" holds AV = 8 bf16 or 4 fp32 values.
+// For a k range of 2 AV, lane l of a wavefront holds the vector of row
+// m = l % 32 at k offset AV * (l / 32) for the A operand, and of column
+// n = l % 32 likewise for B.  For bf16 that vector is exactly the operand of
+// one 32x32x16 MFMA; for fp32 it feeds four 32x32x2 MFMAs, step t taking
+// element t of both vectors.  Either way every product A[m][k] B[k][n] of the
+// range enters the sum once (the fp32 steps visit k in a permuted order,
+// the same on both operands).  Accumulator element v of lane l is
+// C[m][n] with n = l % 32 and m = 8 (v / 4) + 4 (l / 32) + v % 4.
+//
+// LDS tiles are rows of 16-byte chunks with an XOR swizzle on the chunk
+// index (no padding), chosen so that the operand reads (8 rows, one chunk
+// each) and the transposing writes of the staging code spread over the
+// banks.
 #include <algorithm>
 
 #include "device.hpp"
@@ -21,32 +29,24 @@
 
 namespace gt {
 
-typedef short v4s __attribute__((ext_vector_type(4)));
 typedef float v16f __attribute__((ext_vector_type(16)));
+typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
 
 template <typename T> struct Mma;
 template <> struct Mma<bf16_t> {
-  static constexpr int KSTEP = 8, KW = 4;    // k per instruction, k per lane
-  static constexpr int PAD = 8;              // LDS row padding (elements)
-  __device__ static inline v16f mma(const bf16_t *a, const bf16_t *b, v16f c) {
-    const v4s av = *reinterpret_cast<const v4s *>(a);
-    const v4s bv = *reinterpret_cast<const v4s *>(b);
-    return __builtin_amdgcn_mfma_f32_32x32x8bf16_1k(av, bv, c, 0, 0, 0);
+  __device__ static inline v16f mma(const uint4 &a, const uint4 &b, v16f c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(v8bf, a),
+                                                   __builtin_bit_cast(v8bf, b), c, 0, 0, 0);
   }
-  __device__ static inline bf16_t cvt(float x) { return bf16_t{(uint16_t)f32_to_bf16_bits(x)}; }
-  __device__ static inline float val(bf16_t x) { return __uint_as_float((uint32_t)x.bits << 16); }
 };
 template <> struct Mma<float> {
-  static constexpr int KSTEP = 2, KW = 1;
-  static constexpr int PAD = 4;
-  __device__ static inline v16f mma(const float *a, const float *b, v16f c) {
-    return __builtin_amdgcn_mfma_f32_32x32x2f32(*a, *b, c, 0, 0, 0);
+  __device__ static inline v16f mma(const uint4 &a, const uint4 &b, v16f c) {
+    c = __builtin_amdgcn_mfma_f32_32x32x2f32(__uint_as_float(a.x), __uint_as_float(b.x), c, 0, 0, 0);
+    c = __builtin_amdgcn_mfma_f32_32x32x2f32(__uint_as_float(a.y), __uint_as_float(b.y), c, 0, 0, 0);
+    c = __builtin_amdgcn_mfma_f32_32x32x2f32(__uint_as_float(a.z), __uint_as_float(b.z), c, 0, 0, 0);
+    return __builtin_amdgcn_mfma_f32_32x32x2f32(__uint_as_float(a.w), __uint_as_float(b.w), c, 0, 0, 0);
   }
-  __device__ static inline float cvt(float x) { return x; }
-  __device__ static inline float val(float x) { return x; }
 };
-
-constexpr int PKC = 32;  // k chunk staged in LDS
 
 // one 16-byte vector of a row-major operand, zero past the end
 template <typename T>
@@ -54,11 +54,47 @@ __device__ inline uint4 load16(const T *p, bool ok) {
   return ok ? *reinterpret_cast<const uint4 *>(p) : make_uint4(0, 0, 0, 0);
 }
 
+__device__ inline uint32_t u4get(const uint4 &v, int i) {
+  return i == 0 ? v.x : i == 1 ? v.y : i == 2 ? v.z : v.w;
+}
+
+// Transposing store of two consecutive rows r0, r1 (AV columns each) into a
+// [column][k] tile: column c receives the pair (r0[c], r1[c]) at k, k + 1.
+// bf16: one dword per column; fp32: one 8-byte store per column.
+template <typename T>
+__device__ inline void store_pair_t(T *tile, const uint4 &r0, const uint4 &r1,
+                                    int (&off)[16 / sizeof(T)]);
+template <>
+__device__ inline void store_pair_t<bf16_t>(bf16_t *tile, const uint4 &r0, const uint4 &r1,
+                                            int (&off)[8]) {
+#pragma unroll
+  for (int c = 0; c < 8; ++c) {
+    const uint32_t a = u4get(r0, c / 2), b = u4get(r1, c / 2);
+    const uint32_t w = (c & 1) ? ((a >> 16) | (b & 0xffff0000u)) : ((a & 0xffffu) | (b << 16));
+    *reinterpret_cast<uint32_t *>(tile + off[c]) = w;
+  }
+}
+template <>
+__device__ inline void store_pair_t<float>(float *tile, const uint4 &r0, const uint4 &r1,
+                                           int (&off)[4]) {
+#pragma unroll
+  for (int c = 0; c < 4; ++c)
+    *reinterpret_cast<uint2 *>(tile + off[c]) = make_uint2(u4get(r0, c), u4get(r1, c));
+}
+
 // ---------------------------------------------------------------------------
-// row GEMM: C_z[rows, cols] = sum_s A_s[rows, :] op(B_zs) (+ R), with
-// op(W) = W or W^T, every operand [n, d] or [d, d] row-major.
-// grid (ceil(n/128), d/BN, outputs); 4 wavefronts, wavefront w owns rows
-// [32w, 32w+32) of the tile and all BN columns.
+// row GEMM: C_z[rows, :] = sum_s A_s[rows, :] op(W_zs) (+ R), op(W) = W or W^T,
+// every operand [n, D] or [D, D] row-major.
+//
+// A workgroup of 8 wavefronts takes 256 node rows; wavefront w owns rows
+// [32w, 32w + 32) and holds its A strip in registers, loaded straight from
+// memory in the operand layout (lane l: row l % 32, vectors at k = 2 AV c +
+// AV (l / 32)).  op(W) streams through LDS one 32-column tile at a time,
+// stored [n][k], double-buffered: tile t + 1 is fetched into registers while
+// tile t is multiplied.  With one source (NA = 1: the Q/K/V and output
+// projections) each 32x32 result block is written as soon as it is done;
+// with four (NA = 4: the input gradient) the whole row strip accumulates
+// before the write.
 // ---------------------------------------------------------------------------
 struct RowsGemm {
   const void *A[4];
@@ -66,194 +102,376 @@ struct RowsGemm {
   void *C[3];
   const void *R;     // residual added to C[0] (nullable)
   int64_t n;
-  int d, na;
+  int d, na, nout;
 };
 
-template <typename T, int BN, bool TRANSB>
-__global__ __launch_bounds__(256) void k_gemm_rows(RowsGemm g) {
-  using M = Mma<T>;
-  constexpr int BM = 128, LD = PKC + M::PAD, AV = 16 / sizeof(T);
-  __shared__ __align__(16) T As[BM * LD];
-  __shared__ __align__(16) T Bs[BN * LD];
-  const int tid = threadIdx.x, lane = tid & (WAVE - 1), w = tid / WAVE;
-  const int64_t m0 = (int64_t)blockIdx.x * BM;
-  const int n0 = blockIdx.y * BN, z = blockIdx.z, d = g.d;
-  const int koff = M::KW * (lane / 32);
-  v16f acc[BN / 32];
+constexpr int RG_WAVES = 8, RG_THREADS = RG_WAVES * WAVE, RG_ROWS = RG_WAVES * 32;
+
+// chunk swizzle of the [32][D] weight tile: row n, chunk q -> element offset
+template <int D, int AV>
+__device__ inline int btile_off(int n, int q) {
+  return n * D + ((q ^ ((n ^ (n >> 3)) & 7)) * AV);
+}
+
+// store the 32 x 32 block (m0.., col0..) of acc to C (+ residual R)
+template <typename T>
+__device__ inline void store_block(T *C, const T *R, int64_t m0, int col0, int D, int64_t n,
+                                   const v16f &acc, int lane);
+
+template <>
+__device__ inline void store_block<float>(float *C, const float *R, int64_t m0, int col0, int D,
+                                          int64_t n, const v16f &acc, int lane) {
+  const int h = lane / 32, col = col0 + lane % 32;
 #pragma unroll
-  for (int j = 0; j < BN / 32; ++j)
-#pragma unroll
-    for (int v = 0; v < 16; ++v) acc[j][v] = 0.f;
-  for (int s = 0; s < g.na; ++s) {
-    const T *A = (const T *)g.A[s];
-    const T *B = (const T *)g.B[z][s];
-    for (int k0 = 0; k0 < d; k0 += PKC) {
-      __syncthreads();
-      for (int i = tid; i < BM * PKC / AV; i += 256) {
-        const int r = i / (PKC / AV), c = (i % (PKC / AV)) * AV;
-        const int64_t row = m0 + r;
-        *reinterpret_cast<uint4 *>(&As[r * LD + c]) = load16(A + row * d + k0 + c, row < g.n);
-      }
-      if constexpr (TRANSB) {   // B[k][n] = W[n][k]: rows of W are k-contiguous
-        for (int i = tid; i < BN * PKC / AV; i += 256) {
-          const int nn = i / (PKC / AV), c = (i % (PKC / AV)) * AV;
-          *reinterpret_cast<uint4 *>(&Bs[nn * LD + c]) = load16(B + (int64_t)(n0 + nn) * d + k0 + c, true);
-        }
-      } else {                  // B[k][n] = W[k][n]: scatter into Bs[n][k]
-        for (int i = tid; i < PKC * BN / AV; i += 256) {
-          const int kk = i / (BN / AV), c = (i % (BN / AV)) * AV;
-          const uint4 v = load16(B + (int64_t)(k0 + kk) * d + n0 + c, true);
-          const T *e = reinterpret_cast<const T *>(&v);
-#pragma unroll
-          for (int q = 0; q < AV; ++q) Bs[(c + q) * LD + kk] = e[q];
-        }
-      }
-      __syncthreads();
-#pragma unroll
-      for (int kk = 0; kk < PKC; kk += M::KSTEP) {
-        const T *a = &As[(32 * w + lane % 32) * LD + kk + koff];
-#pragma unroll
-        for (int j = 0; j < BN / 32; ++j)
-          acc[j] = M::mma(a, &Bs[(32 * j + lane % 32) * LD + kk + koff], acc[j]);
-      }
-    }
-  }
-  T *C = (T *)g.C[z];
-  const T *R = (z == 0) ? (const T *)g.R : nullptr;
-#pragma unroll
-  for (int j = 0; j < BN / 32; ++j) {
-    const int col = n0 + 32 * j + lane % 32;
-#pragma unroll
-    for (int v = 0; v < 16; ++v) {
-      const int64_t row = m0 + 32 * w + 8 * (v / 4) + 4 * (lane / 32) + v % 4;
-      if (row < g.n) {
-        float x = acc[j][v];
-        if (R) x += M::val(R[row * d + col]);
-        C[row * d + col] = M::cvt(x);
-      }
+  for (int v = 0; v < 16; ++v) {
+    const int64_t row = m0 + 8 * (v / 4) + 4 * h + v % 4;
+    if (row < n) {
+      float x = acc[v];
+      if (R) x += R[row * D + col];
+      C[row * D + col] = x;
     }
   }
 }
 
+// bf16: neighbouring lanes swap one element so that each lane writes two
+// adjacent columns of one row as a dword.
+template <>
+__device__ inline void store_block<bf16_t>(bf16_t *C, const bf16_t *R, int64_t m0, int col0,
+                                           int D, int64_t n, const v16f &acc, int lane) {
+  const int h = lane / 32, nn = lane % 32, odd = nn & 1;
+  const int col = col0 + nn - odd;
+#pragma unroll
+  for (int v = 0; v < 16; v += 2) {
+    const float give = odd ? acc[v] : acc[v + 1];
+    const float got = dpp<DPP_QUAD_XOR1>(give);
+    const float lo = odd ? got : acc[v], hi = odd ? acc[v + 1] : got;
+    const int64_t row = m0 + 8 * (v / 4) + 4 * h + v % 4 + odd;
+    if (row < n) {
+      float x0 = lo, x1 = hi;
+      if (R) {
+        const uint32_t r = *reinterpret_cast<const uint32_t *>(R + row * D + col);
+        x0 += __uint_as_float(r << 16);
+        x1 += __uint_as_float(r & 0xffff0000u);
+      }
+      *reinterpret_cast<uint32_t *>(C + row * D + col) =
+          f32_to_bf16_bits(x0) | (f32_to_bf16_bits(x1) << 16);
+    }
+  }
+}
+
+template <typename T, int D, bool TRANSB, int NA>
+__global__ __launch_bounds__(RG_THREADS) void k_gemm_rows(RowsGemm g) {
+  using M = Mma<T>;
+  constexpr int AV = 16 / sizeof(T);          // elements per vector
+  constexpr int CH = D / (2 * AV);            // k ranges of 2 AV
+  constexpr int J = D / 32;                   // 32-column blocks
+  constexpr int TILE = 32 * D;                // elements of one weight tile
+  // staging: each thread moves SV vectors of a tile (SV = 0.5: half the threads)
+  constexpr int TV = TILE / AV;
+  constexpr int SV = TV >= RG_THREADS ? TV / RG_THREADS : 1;
+  constexpr int SU = TRANSB ? SV : (SV + 1) / 2;   // units: vectors or row pairs
+  __shared__ __align__(16) T Bs[2][TILE];
+  const int tid = threadIdx.x, lane = tid & (WAVE - 1), w = tid / WAVE, h = lane / 32;
+  const int64_t m0 = (int64_t)blockIdx.x * RG_ROWS + 32 * w;
+  const int64_t arow = m0 + lane % 32;
+  const bool arow_ok = arow < g.n;
+  const int nout = NA == 1 ? g.nout : 1;
+  const int ntiles = (NA == 1 ? nout : NA) * J;
+
+  // fetch tile t of the sequence (source s = t / J for NA = 4, output z =
+  // t / J for NA = 1; columns 32 (t % J) ..) into registers
+  uint4 st[TRANSB ? SV : 2 * SU];
+  auto fetch = [&](int t) {
+    const int zs = t / J, j = t % J;
+    const T *W = (const T *)(NA == 1 ? g.B[zs][0] : g.B[0][zs]);
+    if constexpr (TRANSB) {      // tile[n][k] = W[32 j + n][k]
+#pragma unroll
+      for (int i = 0; i < SV; ++i) {
+        const int u = tid + i * RG_THREADS;
+        const int q = u % (D / AV), nn = u / (D / AV);
+        st[i] = load16(W + (int64_t)(32 * j + nn) * D + q * AV, u < TV);
+      }
+    } else {                     // tile[n][k] = W[k][32 j + n], rows k, k + 1
+#pragma unroll
+      for (int i = 0; i < SU; ++i) {
+        const int u = tid + i * RG_THREADS;
+        const int ng = u % (32 / AV), kp = u / (32 / AV);
+        const bool ok = u < TV / 2;
+        st[2 * i] = load16(W + (int64_t)(2 * kp) * D + 32 * j + ng * AV, ok);
+        st[2 * i + 1] = load16(W + (int64_t)(2 * kp + 1) * D + 32 * j + ng * AV, ok);
+      }
+    }
+  };
+  auto put = [&](T *tile) {
+    if constexpr (TRANSB) {
+#pragma unroll
+      for (int i = 0; i < SV; ++i) {
+        const int u = tid + i * RG_THREADS;
+        if (u < TV)
+          *reinterpret_cast<uint4 *>(tile + btile_off<D, AV>(u / (D / AV), u % (D / AV))) = st[i];
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < SU; ++i) {
+        const int u = tid + i * RG_THREADS;
+        if (u < TV / 2) {
+          const int ng = u % (32 / AV), kp = u / (32 / AV), k0 = 2 * kp;
+          int off[AV];
+#pragma unroll
+          for (int c = 0; c < AV; ++c) off[c] = btile_off<D, AV>(ng * AV + c, k0 / AV) + k0 % AV;
+          store_pair_t<T>(tile, st[2 * i], st[2 * i + 1], off);
+        }
+      }
+    }
+  };
+
+  uint4 a[CH];
+  auto load_a = [&](int s) {
+    const T *A = (const T *)g.A[s];
+#pragma unroll
+    for (int c = 0; c < CH; ++c) a[c] = load16(A + arow * D + c * 2 * AV + h * AV, arow_ok);
+  };
+
+  v16f acc[NA == 1 ? 1 : J];
+#pragma unroll
+  for (int j = 0; j < (NA == 1 ? 1 : J); ++j)
+#pragma unroll
+    for (int v = 0; v < 16; ++v) acc[j][v] = 0.f;
+
+  fetch(0);
+  load_a(0);
+  put(Bs[0]);
+  __syncthreads();
+  for (int t = 0; t < ntiles; ++t) {
+    const int zs = t / J, j = t % J;
+    if (t + 1 < ntiles) fetch(t + 1);
+    if (NA > 1 && j == 0 && zs > 0) load_a(zs);
+    const T *tile = Bs[t & 1];
+    v16f &c_acc = acc[NA == 1 ? 0 : j];
+#pragma unroll
+    for (int c = 0; c < CH; ++c) {
+      const uint4 b = *reinterpret_cast<const uint4 *>(tile + btile_off<D, AV>(lane % 32, 2 * c + h));
+      c_acc = M::mma(a[c], b, c_acc);
+    }
+    if constexpr (NA == 1) {
+      store_block<T>((T *)g.C[zs], zs == 0 ? (const T *)g.R : nullptr, m0, 32 * j, D, g.n,
+                     c_acc, lane);
+#pragma unroll
+      for (int v = 0; v < 16; ++v) c_acc[v] = 0.f;
+    }
+    if (t + 1 < ntiles) put(Bs[(t + 1) & 1]);
+    __syncthreads();
+  }
+  if constexpr (NA > 1) {
+#pragma unroll
+    for (int j = 0; j < J; ++j)
+      store_block<T>((T *)g.C[0], nullptr, m0, 32 * j, D, g.n, acc[j], lane);
+  }
+}
+
 // ---------------------------------------------------------------------------
-// weight gradient: part[s][chunk] = X[rows of chunk]^T G_s[rows of chunk]
-// (an MT x BN tile of the [d, d] result per workgroup), then a fixed-order sum
-// over chunks.  grid (chunks, tiles, grads); MT/32 wavefronts.
+// weight gradient: dW_s = X^T G_s, a contraction over the n node rows.
+// The rows are cut into `slots` contiguous ranges; workgroup (s, slot)
+// computes the whole [D, D] product of its range for gradient s into
+// part[s][slot], and a second kernel sums the slots in slot order
+// (deterministic, no atomics).  Per step a workgroup stages KT = 32 rows
+// of X and G_s into LDS transposed to [column][row] (two rows per thread,
+// swapped into column pairs in registers), the next step's rows already in
+// flight, and its wavefronts each multiply a (32 MB) x (32 NB) block.
+// Workgroups of one slot sit eight block indices apart, so the four that
+// share X rows land on the same XCD (and L2).
 // ---------------------------------------------------------------------------
 struct WgradGemm {
   const void *X;
   const void *G[4];
-  float *part;       // [grads][chunks][d][d]
+  float *part;       // [grads][slots][d][d]
   float *dW[4];
-  int64_t n, rows_per_chunk, chunks;
-  int d, ngrad;
+  int64_t n, rows_per_slot;
+  int slots, d, ngrad;
 };
 
-template <typename T, int MT, int BN>
-__global__ __launch_bounds__(MT * 2) void k_gemm_wgrad(WgradGemm g) {
-  using M = Mma<T>;
-  constexpr int NT = MT * 2, LD = PKC + M::PAD, AV = 16 / sizeof(T);
-  __shared__ __align__(16) T As[MT * LD];
-  __shared__ __align__(16) T Bs[BN * LD];
-  const int tid = threadIdx.x, lane = tid & (WAVE - 1), w = tid / WAVE;
-  const int d = g.d, tiles_n = d / BN;
-  const int m0 = (blockIdx.y / tiles_n) * MT, n0 = (blockIdx.y % tiles_n) * BN, s = blockIdx.z;
-  const int64_t r0 = (int64_t)blockIdx.x * g.rows_per_chunk;
-  const int64_t r1 = r0 + g.rows_per_chunk < g.n ? r0 + g.rows_per_chunk : g.n;
-  const T *X = (const T *)g.X, *G = (const T *)g.G[s];
-  const int koff = M::KW * (lane / 32);
-  v16f acc[BN / 32];
-#pragma unroll
-  for (int j = 0; j < BN / 32; ++j)
-#pragma unroll
-    for (int v = 0; v < 16; ++v) acc[j][v] = 0.f;
-  for (int64_t k0 = r0; k0 < r1; k0 += PKC) {
-    __syncthreads();
-    // As[m][k] = X[k0 + k][m0 + m], Bs[n][k] = G[k0 + k][n0 + n]; rows past r1 are 0
-    for (int i = tid; i < PKC * MT / AV; i += NT) {
-      const int kk = i / (MT / AV), c = (i % (MT / AV)) * AV;
-      const int64_t row = k0 + kk;
-      const uint4 v = load16(X + row * d + m0 + c, row < r1);
-      const T *e = reinterpret_cast<const T *>(&v);
-#pragma unroll
-      for (int q = 0; q < AV; ++q) As[(c + q) * LD + kk] = e[q];
-    }
-    for (int i = tid; i < PKC * BN / AV; i += NT) {
-      const int kk = i / (BN / AV), c = (i % (BN / AV)) * AV;
-      const int64_t row = k0 + kk;
-      const uint4 v = load16(G + row * d + n0 + c, row < r1);
-      const T *e = reinterpret_cast<const T *>(&v);
-#pragma unroll
-      for (int q = 0; q < AV; ++q) Bs[(c + q) * LD + kk] = e[q];
-    }
-    __syncthreads();
-#pragma unroll
-    for (int kk = 0; kk < PKC; kk += M::KSTEP) {
-      const T *a = &As[(32 * w + lane % 32) * LD + kk + koff];
-#pragma unroll
-      for (int j = 0; j < BN / 32; ++j)
-        acc[j] = M::mma(a, &Bs[(32 * j + lane % 32) * LD + kk + koff], acc[j]);
-    }
-  }
-  float *P = g.part + ((int64_t)s * g.chunks + blockIdx.x) * d * d;
-#pragma unroll
-  for (int j = 0; j < BN / 32; ++j) {
-    const int col = n0 + 32 * j + lane % 32;
-#pragma unroll
-    for (int v = 0; v < 16; ++v) {
-      const int row = m0 + 32 * w + 8 * (v / 4) + 4 * (lane / 32) + v % 4;
-      P[(int64_t)row * d + col] = acc[j][v];
-    }
-  }
+constexpr int WG_KT = 32;
+
+template <int D> struct WgradShape;
+template <> struct WgradShape<64> { static constexpr int WM = 2, WN = 2, MB = 1, NB = 1; };
+template <> struct WgradShape<128> { static constexpr int WM = 4, WN = 2, MB = 1, NB = 2; };
+template <> struct WgradShape<256> { static constexpr int WM = 4, WN = 2, MB = 2, NB = 4; };
+
+// swizzled [column][KT] tile: column m, chunk q -> element offset
+template <typename T>
+__device__ inline int wtile_off(int m, int q) {
+  constexpr int AV = 16 / sizeof(T), NCH = WG_KT / AV;           // chunks per row
+  constexpr int RS = sizeof(T) == 2 ? 1 : 0;                    // rows per 128 B = 2^RS
+  constexpr int LG = NCH == 4 ? 2 : 3;
+  return m * WG_KT + ((q ^ (((m >> RS) ^ (m >> (RS + LG))) & (NCH - 1))) * AV);
 }
 
-// dW_s[i] = sum over chunks, in chunk order, of part[s][chunk][i]
+template <typename T, int D>
+__global__ __launch_bounds__(WgradShape<D>::WM * WgradShape<D>::WN * WAVE)
+void k_gemm_wgrad(WgradGemm g) {
+  using M = Mma<T>;
+  using S = WgradShape<D>;
+  constexpr int NT = S::WM * S::WN * WAVE;
+  constexpr int AV = 16 / sizeof(T);
+  constexpr int CH = WG_KT / (2 * AV);          // k ranges per step
+  constexpr int UOP = (WG_KT / 2) * (D / AV);   // row-pair units per operand
+  constexpr int SU = (2 * UOP + NT - 1) / NT;   // units per thread
+  constexpr int TILE = D * WG_KT;
+  __shared__ __align__(16) T Xs[TILE];
+  __shared__ __align__(16) T Gs[TILE];
+  const int tid = threadIdx.x, lane = tid & (WAVE - 1), w = tid / WAVE, h = lane / 32;
+  const int wm = w % S::WM, wn = w / S::WM;
+  const int b = blockIdx.x;
+  const int s = (b / 8) % 4, slot = (b % 8) + 8 * (b / 32);
+  if (s >= g.ngrad || slot >= g.slots) return;   // grid is exactly slots * 4; kept for safety
+  const int64_t r0 = (int64_t)slot * g.rows_per_slot;
+  const int64_t r1 = std::min<int64_t>(r0 + g.rows_per_slot, g.n);
+  const T *X = (const T *)g.X, *G = (const T *)g.G[s];
+
+  uint4 st[2 * SU];
+  // unit u: operand u / UOP, column group mg, row pair kp of the step
+  auto unit = [&](int u, int &op, int &mg, int &kp) {
+    const int v = u % UOP;
+    op = u / UOP;
+    const int lo = v % 4, rest = v / 4;
+    mg = rest % (D / AV);
+    kp = lo + 4 * (rest / (D / AV));
+  };
+  auto fetch = [&](int64_t k0) {
+#pragma unroll
+    for (int i = 0; i < SU; ++i) {
+      const int u = tid + i * NT;
+      int op, mg, kp;
+      unit(u, op, mg, kp);
+      const T *P = op == 0 ? X : G;
+      const int64_t row = k0 + 2 * kp;
+      const bool ok = u < 2 * UOP;
+      st[2 * i] = load16(P + row * D + mg * AV, ok && row < r1);
+      st[2 * i + 1] = load16(P + (row + 1) * D + mg * AV, ok && row + 1 < r1);
+    }
+  };
+  auto put = [&]() {
+#pragma unroll
+    for (int i = 0; i < SU; ++i) {
+      const int u = tid + i * NT;
+      if (u < 2 * UOP) {
+        int op, mg, kp;
+        unit(u, op, mg, kp);
+        const int k = 2 * kp;
+        int off[AV];
+#pragma unroll
+        for (int c = 0; c < AV; ++c) off[c] = wtile_off<T>(mg * AV + c, k / AV) + k % AV;
+        store_pair_t<T>(op == 0 ? Xs : Gs, st[2 * i], st[2 * i + 1], off);
+      }
+    }
+  };
+
+  v16f acc[S::MB][S::NB];
+#pragma unroll
+  for (int i = 0; i < S::MB; ++i)
+#pragma unroll
+    for (int j = 0; j < S::NB; ++j)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
+
+  if (r0 < r1) fetch(r0);
+  for (int64_t k0 = r0; k0 < r1; k0 += WG_KT) {
+    __syncthreads();
+    put();
+    __syncthreads();
+    if (k0 + WG_KT < r1) fetch(k0 + WG_KT);
+#pragma unroll
+    for (int c = 0; c < CH; ++c) {
+      uint4 av[S::MB], bv[S::NB];
+#pragma unroll
+      for (int i = 0; i < S::MB; ++i)
+        av[i] = *reinterpret_cast<const uint4 *>(
+            Xs + wtile_off<T>(32 * (wm * S::MB + i) + lane % 32, 2 * c + h));
+#pragma unroll
+      for (int j = 0; j < S::NB; ++j)
+        bv[j] = *reinterpret_cast<const uint4 *>(
+            Gs + wtile_off<T>(32 * (wn * S::NB + j) + lane % 32, 2 * c + h));
+#pragma unroll
+      for (int i = 0; i < S::MB; ++i)
+#pragma unroll
+        for (int j = 0; j < S::NB; ++j) acc[i][j] = M::mma(av[i], bv[j], acc[i][j]);
+    }
+  }
+  float *P = g.part + ((int64_t)s * g.slots + slot) * D * D;
+#pragma unroll
+  for (int i = 0; i < S::MB; ++i)
+#pragma unroll
+    for (int j = 0; j < S::NB; ++j) {
+      const int col = 32 * (wn * S::NB + j) + lane % 32;
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const int row = 32 * (wm * S::MB + i) + 8 * (v / 4) + 4 * h + v % 4;
+        P[(int64_t)row * D + col] = acc[i][j][v];
+      }
+    }
+}
+
+// dW_s[i] = sum over slots, in slot order, of part[s][slot][i]
 __global__ void k_wgrad_reduce(WgradGemm g) {
   const int64_t dd = (int64_t)g.d * g.d;
   const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (t >= dd * g.ngrad) return;
   const int s = (int)(t / dd);
   const int64_t i = t % dd;
-  const float *p = g.part + (int64_t)s * g.chunks * dd + i;
+  const float *p = g.part + (int64_t)s * g.slots * dd + i;
   float x = 0.f;
-  for (int64_t c = 0; c < g.chunks; ++c) x += p[c * dd];
+  for (int c = 0; c < g.slots; ++c) x += p[c * dd];
   g.dW[s][i] = x;
 }
 
 // ---------------------------------------------------------------------------
 // host side
 // ---------------------------------------------------------------------------
-constexpr int64_t WGRAD_ROWS = 8192;   // node rows per weight-gradient chunk
+// Slots of the weight gradient: a multiple of 8, at most 64 (one workgroup
+// per CU at d = 256) or 128, and no more than the 32-row steps of n.
+int wgrad_slots(int64_t n, int d) {
+  const int64_t cap = d >= 256 ? 64 : 128;
+  const int64_t steps = cdiv(std::max<int64_t>(n, 1), WG_KT);
+  return (int)std::min<int64_t>(cap, cdiv(steps, 8) * 8);
+}
 
-int64_t wgrad_chunks(int64_t n) { return n > 0 ? cdiv(n, WGRAD_ROWS) : 0; }
+int64_t wgrad_rows_per_slot(int64_t n, int slots) {
+  return cdiv(cdiv(std::max<int64_t>(n, 1), slots), WG_KT) * WG_KT;
+}
 
-template <typename T, bool TRANSB>
-static gt_status run_rows(const RowsGemm &g, int nout, hipStream_t st) {
+template <typename T, bool TRANSB, int NA>
+static void launch_rows(const RowsGemm &g, dim3 grid, hipStream_t st) {
+  switch (g.d) {
+    case 64: k_gemm_rows<T, 64, TRANSB, NA><<<grid, RG_THREADS, 0, st>>>(g); break;
+    case 128: k_gemm_rows<T, 128, TRANSB, NA><<<grid, RG_THREADS, 0, st>>>(g); break;
+    default: k_gemm_rows<T, 256, TRANSB, NA><<<grid, RG_THREADS, 0, st>>>(g); break;
+  }
+}
+
+// transb = false: one source (NA = 1); transb = true: four (NA = 4)
+gt_status launch_rows_gemm(gt_dtype dt, RowsGemm g, int nout, bool transb, hipStream_t st) {
   if (g.n == 0) return GT_OK;
-  const unsigned gx = (unsigned)cdiv(g.n, 128);
-  if (g.d == 64) {
-    k_gemm_rows<T, 64, TRANSB><<<dim3(gx, 1, nout), 256, 0, st>>>(g);
+  g.nout = nout;
+  const dim3 grid((unsigned)cdiv(g.n, RG_ROWS));
+  if (dt == GT_F32) {
+    if (transb) launch_rows<float, true, 4>(g, grid, st);
+    else launch_rows<float, false, 1>(g, grid, st);
   } else {
-    k_gemm_rows<T, 128, TRANSB><<<dim3(gx, g.d / 128, nout), 256, 0, st>>>(g);
+    if (transb) launch_rows<bf16_t, true, 4>(g, grid, st);
+    else launch_rows<bf16_t, false, 1>(g, grid, st);
   }
   GT_CHECK_LAUNCH();
   return GT_OK;
 }
 
-gt_status launch_rows_gemm(gt_dtype dt, const RowsGemm &g, int nout, bool transb, hipStream_t st) {
-  if (dt == GT_F32)
-    return transb ? run_rows<float, true>(g, nout, st) : run_rows<float, false>(g, nout, st);
-  return transb ? run_rows<bf16_t, true>(g, nout, st) : run_rows<bf16_t, false>(g, nout, st);
-}
-
 template <typename T>
 static gt_status run_wgrad(WgradGemm &g, hipStream_t st) {
-  if (g.chunks > 0) {
-    if (g.d == 64) {
-      k_gemm_wgrad<T, 64, 64><<<dim3((unsigned)g.chunks, 1, g.ngrad), 128, 0, st>>>(g);
-    } else {
-      const int tiles = (g.d / 128) * (g.d / 128);
-      k_gemm_wgrad<T, 128, 128><<<dim3((unsigned)g.chunks, tiles, g.ngrad), 256, 0, st>>>(g);
+  if (g.n > 0) {
+    const dim3 grid((unsigned)(g.slots * 4));
+    switch (g.d) {
+      case 64: k_gemm_wgrad<T, 64><<<grid, 4 * WAVE, 0, st>>>(g); break;
+      case 128: k_gemm_wgrad<T, 128><<<grid, 8 * WAVE, 0, st>>>(g); break;
+      default: k_gemm_wgrad<T, 256><<<grid, 8 * WAVE, 0, st>>>(g); break;
     }
     GT_CHECK_LAUNCH();
   }
@@ -368,7 +586,7 @@ extern "C" gt_status gt_proj_bwd_data(int64_t n, int32_t d, gt_dtype dt, const v
 
 extern "C" size_t gt_proj_work_bytes(int64_t n, int32_t d) {
   if (n < 0 || d <= 0) return 0;
-  return (size_t)std::max<int64_t>(4 * wgrad_chunks(n) * (int64_t)d * d * 4, 256);
+  return (size_t)std::max<int64_t>(4 * (int64_t)wgrad_slots(n, d) * d * d * 4, 256);
 }
 
 extern "C" gt_status gt_proj_bwd_weight(int64_t n, int32_t d, gt_dtype dt, const void *X,
@@ -395,8 +613,8 @@ extern "C" gt_status gt_proj_bwd_weight(int64_t n, int32_t d, gt_dtype dt, const
   g.X = X;
   g.part = (float *)work;
   g.n = n;
-  g.rows_per_chunk = WGRAD_ROWS;
-  g.chunks = wgrad_chunks(n);
+  g.slots = n > 0 ? wgrad_slots(n, d) : 0;     // n = 0: the sums are empty, dW = 0
+  g.rows_per_slot = n > 0 ? wgrad_rows_per_slot(n, g.slots) : 0;
   g.d = d;
   g.ngrad = 4;
   return launch_wgrad(dt, g, (hipStream_t)stream);

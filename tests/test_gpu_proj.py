@@ -26,7 +26,8 @@ def _abs(x):
 
 
 CASES = [(n, d, dt) for dt in ("f32", "bf16") for n, d in
-         ((1, 64), (100, 128), (128, 256), (1000, 64), (4097, 128), (20000, 256))]
+         ((1, 64), (100, 128), (128, 256), (1000, 64), (4097, 128), (20000, 256),
+          (70001, 128), (50003, 256))]
 
 
 @pytest.mark.parametrize("case", CASES, ids=[f"n{n}-d{d}-{dt}" for n, d, dt in CASES])
@@ -95,3 +96,16 @@ def test_layer(case):
         assert_close(Wd[k].grad, rb["dW" + k], rt, "dW" + k)
     if bias:
         assert_close(bd.grad, rb["dbias"], rt, "dbias", head_axis=1)
+
+
+def test_empty_node_set():
+    """n = 0: the products are empty, the weight gradients exactly zero."""
+    d = 128
+    X = torch.empty((0, d), dtype=torch.float32, device="cuda")
+    W = torch.ones((d, d), dtype=torch.float32, device="cuda")
+    Q, K, V = T.gt_proj_qkv(X, W, W, W)
+    assert Q.shape == (0, d)
+    dX = T.gt_proj_bwd_data(X, X, X, X, W, W, W, W)
+    assert dX.shape == (0, d)
+    for dw in T.gt_proj_bwd_weight(X, X, X, X, X):
+        assert dw.shape == (d, d) and torch.count_nonzero(dw).item() == 0
