@@ -23,6 +23,7 @@
 // each) and the transposing writes of the staging code spread over the
 // banks.
 #include <algorithm>
+#include <type_traits>
 
 #include "device.hpp"
 #include "host.hpp"
@@ -164,7 +165,8 @@ __global__ __launch_bounds__(RG_THREADS) void k_gemm_rows(RowsGemm g) {
   using M = Mma<T>;
   constexpr int AV = 16 / sizeof(T);          // elements per vector
   constexpr int CH = D / (2 * AV);            // k ranges of 2 AV
-  constexpr int J = D / 32;                   // 32-column blocks
+  constexpr int J = D / 32;                   // 32-column blocks (even)
+  static_assert(J % 2 == 0, "tile parity");
   constexpr int TILE = 32 * D;                // elements of one weight tile
   // staging: each thread moves SV vectors of a tile (SV = 0.5: half the threads)
   constexpr int TV = TILE / AV;
@@ -242,30 +244,245 @@ __global__ __launch_bounds__(RG_THREADS) void k_gemm_rows(RowsGemm g) {
   load_a(0);
   put(Bs[0]);
   __syncthreads();
-  for (int t = 0; t < ntiles; ++t) {
-    const int zs = t / J, j = t % J;
-    if (t + 1 < ntiles) fetch(t + 1);
-    if (NA > 1 && j == 0 && zs > 0) load_a(zs);
-    const T *tile = Bs[t & 1];
-    v16f &c_acc = acc[NA == 1 ? 0 : j];
+  // outer loop: output z (NA = 1) or source s (NA = 4); inner: column blocks
+  for (int zs = 0; zs < (NA == 1 ? nout : NA); ++zs) {
+    if (NA > 1 && zs > 0) load_a(zs);
 #pragma unroll
-    for (int c = 0; c < CH; ++c) {
-      const uint4 b = *reinterpret_cast<const uint4 *>(tile + btile_off<D, AV>(lane % 32, 2 * c + h));
-      c_acc = M::mma(a[c], b, c_acc);
-    }
-    if constexpr (NA == 1) {
-      store_block<T>((T *)g.C[zs], zs == 0 ? (const T *)g.R : nullptr, m0, 32 * j, D, g.n,
-                     c_acc, lane);
+    for (int j = 0; j < J; ++j) {
+      const int t = zs * J + j;          // J is even: tile t sits in Bs[j & 1]
+      if (t + 1 < ntiles) fetch(t + 1);
+      v16f &c_acc = acc[NA == 1 ? 0 : j];
 #pragma unroll
-      for (int v = 0; v < 16; ++v) c_acc[v] = 0.f;
+      for (int c = 0; c < CH; ++c) {
+        const uint4 b = *reinterpret_cast<const uint4 *>(Bs[j & 1] + btile_off<D, AV>(lane % 32, 2 * c + h));
+        c_acc = M::mma(a[c], b, c_acc);
+      }
+      if constexpr (NA == 1) {
+        store_block<T>((T *)g.C[zs], zs == 0 ? (const T *)g.R : nullptr, m0, 32 * j, D, g.n,
+                       c_acc, lane);
+#pragma unroll
+        for (int v = 0; v < 16; ++v) c_acc[v] = 0.f;
+      }
+      if (t + 1 < ntiles) put(Bs[(j + 1) & 1]);
+      __syncthreads();
     }
-    if (t + 1 < ntiles) put(Bs[(t + 1) & 1]);
-    __syncthreads();
   }
   if constexpr (NA > 1) {
 #pragma unroll
     for (int j = 0; j < J; ++j)
       store_block<T>((T *)g.C[0], nullptr, m0, 32 * j, D, g.n, acc[j], lane);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// one-source row GEMM with the weight resident in LDS: C_z = A W_z (+ R).
+//
+// Used where W fits in LDS (D * D elements of at most 128 KB: bf16 up to
+// D = 256, fp32 up to D = 128).  A workgroup of 8 wavefronts stages one W_z
+// once, as [n][k] with the chunk swizzle, and its wavefronts then run
+// without barriers: each takes 32-row strips of A in turn and holds the
+// strip in registers (operand layout as above) while the next strip's loads
+// are in flight; for each 32-column block it runs CH MFMAs with the strip as
+// the B operand and the weight rows as A, so that lane l ends up with row
+// l % 32 and columns 8 g + 4 (l / 32) + i of the block (g, i < 4): four
+// contiguous values, written as one 8- (bf16) or 16-byte (fp32) store.  The
+// residual of a block is fetched one or two blocks ahead.  Every global
+// access goes through a buffer resource bounded to the strip, so rows past
+// n read as zero and their stores are dropped without a branch (which also
+// keeps the memory counters exact).  Workgroups that share strips for
+// different z sit eight block indices apart (same XCD, same L2).
+// ---------------------------------------------------------------------------
+constexpr int RR_WAVES = 8, RR_THREADS = RR_WAVES * WAVE;
+constexpr uint32_t BUF_WORD3 = 0x00020000u;   // raw buffer, 32-bit elements (gfx9 layout)
+
+__device__ inline __amdgpu_buffer_rsrc_t strip_rsrc(const void *base, int64_t row0, int64_t n,
+                                                    int row_bytes) {
+  const int64_t rows = row0 < n ? std::min<int64_t>(32, n - row0) : 0;
+  const char *p = (const char *)base + (row0 < n ? row0 : 0) * row_bytes;
+  return __builtin_amdgcn_make_buffer_rsrc((void *)p, 0, (int)(rows * row_bytes), BUF_WORD3);
+}
+
+// float32 -> bfloat16 bits, nearest even, without a branch (NaN stays NaN)
+__device__ inline uint32_t bf16_rne(float f) {
+  const uint32_t u = __float_as_uint(f);
+  const uint32_t r = (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
+  return (u & 0x7fffffffu) > 0x7f800000u ? ((u >> 16) | 0x40u) : r;
+}
+
+// the four outputs of a lane in one 32x32 block, as stored
+template <typename T> struct OutVec;
+template <> struct OutVec<float> {
+  typedef uint4 type;
+  __device__ static inline type load(__amdgpu_buffer_rsrc_t r, int o) {
+    return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, o, 0, 0));
+  }
+  __device__ static inline void add(float (&x)[4], const type &v) {
+    x[0] += __uint_as_float(v.x); x[1] += __uint_as_float(v.y);
+    x[2] += __uint_as_float(v.z); x[3] += __uint_as_float(v.w);
+  }
+  __device__ static inline void store(__amdgpu_buffer_rsrc_t r, int o, const float (&x)[4]) {
+    const uint4 v = make_uint4(__float_as_uint(x[0]), __float_as_uint(x[1]),
+                               __float_as_uint(x[2]), __float_as_uint(x[3]));
+    __builtin_amdgcn_raw_buffer_store_b128(
+        __builtin_bit_cast(decltype(__builtin_amdgcn_raw_buffer_load_b128(r, 0, 0, 0)), v), r, o, 0, 0);
+  }
+};
+template <> struct OutVec<bf16_t> {
+  typedef uint2 type;
+  __device__ static inline type load(__amdgpu_buffer_rsrc_t r, int o) {
+    return __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(r, o, 0, 0));
+  }
+  __device__ static inline void add(float (&x)[4], const type &v) {
+    x[0] += __uint_as_float(v.x << 16); x[1] += __uint_as_float(v.x & 0xffff0000u);
+    x[2] += __uint_as_float(v.y << 16); x[3] += __uint_as_float(v.y & 0xffff0000u);
+  }
+  __device__ static inline void store(__amdgpu_buffer_rsrc_t r, int o, const float (&x)[4]) {
+    const uint2 v = make_uint2(bf16_rne(x[0]) | (bf16_rne(x[1]) << 16),
+                               bf16_rne(x[2]) | (bf16_rne(x[3]) << 16));
+    __builtin_amdgcn_raw_buffer_store_b64(
+        __builtin_bit_cast(decltype(__builtin_amdgcn_raw_buffer_load_b64(r, 0, 0, 0)), v), r, o, 0, 0);
+  }
+};
+
+// chunk swizzle of the resident weight: the same for rows n and n + 32, so
+// that a lane's read offsets do not depend on the column block
+__device__ inline int rsw(int n) { return (n ^ ((n >> 3) & 3)) & 7; }
+
+template <typename T, int D, bool RESID, int NZ>
+__global__ __launch_bounds__(RR_THREADS) void k_rows_resident(RowsGemm g, int groups) {
+  using M = Mma<T>;
+  using O = OutVec<T>;
+  constexpr int AV = 16 / sizeof(T), CH = D / (2 * AV), J = D / 32, RB = D * (int)sizeof(T);
+  constexpr int UNITS = (D / 2) * (D / AV);      // (row pair, column group) units of W
+  __shared__ __align__(16) T Ws[NZ * D * D];
+  // the wavefront index is uniform: say so, so that strip addresses and the
+  // buffer resources built from them live in scalar registers
+  const int tid = threadIdx.x, lane = tid & (WAVE - 1), h = lane / 32;
+  const int w = __builtin_amdgcn_readfirstlane(tid / WAVE);
+  // NZ = 1: workgroups split the outputs (z = slot % nout); NZ > 1: every
+  // workgroup holds all NZ weights and writes every output of its strips
+  const int nsplit = NZ == 1 ? g.nout : 1;
+  const int b = blockIdx.x, xcd = b % 8, slot = b / 8;
+  const int zs = slot % nsplit, group = slot / nsplit;
+  // stage W_z: Ws[z][n][k] = W_z[k][n]
+  for (int zz = 0; zz < NZ; ++zz) {
+    const T *W = (const T *)g.B[NZ == 1 ? zs : zz][0];
+    T *Wz = Ws + zz * D * D;
+    for (int u = tid; u < UNITS; u += RR_THREADS) {
+      const int ng = u % (D / AV), kp = u / (D / AV), k0 = 2 * kp;
+      const uint4 r0 = *reinterpret_cast<const uint4 *>(W + (int64_t)k0 * D + ng * AV);
+      const uint4 r1 = *reinterpret_cast<const uint4 *>(W + (int64_t)(k0 + 1) * D + ng * AV);
+      int off[AV];
+#pragma unroll
+      for (int c = 0; c < AV; ++c) {
+        const int nn = ng * AV + c;
+        off[c] = nn * D + (((k0 / AV) ^ rsw(nn)) * AV) + k0 % AV;
+      }
+      store_pair_t<T>(Wz, r0, r1, off);
+    }
+  }
+  __syncthreads();
+  const int64_t strips = (g.n + 31) / 32;
+  const int64_t stride = (int64_t)8 * groups * RR_WAVES;
+  const T *A = (const T *)g.A[0];
+  const T *R = (const T *)g.R;
+  const int aoff = (lane % 32) * RB + h * 16;                  // lane's first A vector
+  const int ooff = (lane % 32) * RB + 4 * h * (int)sizeof(T);  // lane's first output
+  int woff[4];                                                 // lane's weight chunks
+#pragma unroll
+  for (int c4 = 0; c4 < 4; ++c4) woff[c4] = (lane % 32) * D + (((2 * c4 + h) ^ rsw(lane % 32)) * AV);
+  // A strips: the next strip's loads go out before this strip's stores, so
+  // that waiting for them (the memory counter is in order) never waits for
+  // stores.  Two register sets alternate (the loop body is two strips), and
+  // everything inside a strip is unrolled so that the counter waits are exact.
+  const int64_t q0 = ((int64_t)group * 8 + xcd) * RR_WAVES + w;
+  auto load_strip = [&](uint4 (&dst)[CH], int64_t q) {
+    const auto ra = strip_rsrc(A, 32 * q, g.n, RB);
+#pragma unroll
+    for (int c = 0; c < CH; ++c)
+      dst[c] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(ra, aoff + 32 * c, 0, 0));
+  };
+  auto run_strip = [&](const uint4 (&a)[CH], uint4 (&next)[CH], int64_t q) {
+    load_strip(next, q + stride);
+    const int64_t row0 = 32 * q;
+    const auto rr = strip_rsrc(RESID ? (const void *)R : g.C[0], row0, g.n, RB);
+    // residual of block j, fetched RD blocks ahead (fp32 blocks take twice
+    // the registers, so they look one block ahead instead of two)
+    constexpr int RD = sizeof(T) == 4 ? 1 : 2;
+    typename O::type rv[RESID ? J : 1][4];
+    auto fetch_r = [&](int j) {
+#pragma unroll
+      for (int gq = 0; gq < 4; ++gq)
+        rv[j][gq] = O::load(rr, ooff + (32 * j + 8 * gq) * (int)sizeof(T));
+    };
+    if constexpr (RESID) {
+#pragma unroll
+      for (int j = 0; j < RD && j < J; ++j) fetch_r(j);
+    }
+#pragma unroll
+    for (int t = 0; t < NZ * J; ++t) {
+      const int z = t / J, j = t % J;
+      const auto rc = strip_rsrc(g.C[NZ == 1 ? zs : z], row0, g.n, RB);
+      // keep each block's weight reads in place (hoisting them all would need
+      // D * D / 64 registers per lane)
+      asm volatile("" ::: "memory");
+      if constexpr (RESID) {
+        if (j + RD < J) fetch_r(j + RD);
+      }
+      v16f acc;
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[v] = 0.f;
+      const T *wrow = Ws + (z * D + 32 * j) * D;
+#pragma unroll
+      for (int c = 0; c < CH; ++c) {
+        // at most 8 weight vectors in flight per wavefront
+        if (c % 8 == 0 && c > 0) asm volatile("" ::: "memory");
+        // chunk 2c + h of row 32 j + m: its low 3 bits are swizzled, the rest
+        // is a constant offset
+        const uint4 wv = *reinterpret_cast<const uint4 *>(wrow + woff[c % 4] + (c / 4) * 8 * AV);
+        acc = M::mma(wv, a[c], acc);
+      }
+      if constexpr (sizeof(T) == 4) {
+#pragma unroll
+        for (int gq = 0; gq < 4; ++gq) {
+          float x[4] = {acc[4 * gq], acc[4 * gq + 1], acc[4 * gq + 2], acc[4 * gq + 3]};
+          if constexpr (RESID) O::add(x, rv[j][gq]);
+          O::store(rc, ooff + (32 * j + 8 * gq) * (int)sizeof(T), x);
+        }
+      } else {
+        // bf16: pack each group of four, then lanes l and l ^ 32 trade one
+        // group per pair so that each writes eight adjacent columns (16 B):
+        // lane half 0 columns 16 p .. 16 p + 7, half 1 the next eight
+        uint2 pk[4];
+#pragma unroll
+        for (int gq = 0; gq < 4; ++gq) {
+          float x[4] = {acc[4 * gq], acc[4 * gq + 1], acc[4 * gq + 2], acc[4 * gq + 3]};
+          if constexpr (RESID) O::add(x, rv[j][gq]);
+          pk[gq] = make_uint2(bf16_rne(x[0]) | (bf16_rne(x[1]) << 16),
+                              bf16_rne(x[2]) | (bf16_rne(x[3]) << 16));
+        }
+#pragma unroll
+        for (int pp = 0; pp < 2; ++pp) {
+          const uint2 mine = h ? pk[2 * pp + 1] : pk[2 * pp];
+          const uint2 give = h ? pk[2 * pp] : pk[2 * pp + 1];
+          const uint2 got = make_uint2((uint32_t)__shfl_xor((int)give.x, 32),
+                                       (uint32_t)__shfl_xor((int)give.y, 32));
+          const uint4 v = h ? make_uint4(got.x, got.y, mine.x, mine.y)
+                            : make_uint4(mine.x, mine.y, got.x, got.y);
+          const int o = (lane % 32) * RB + (32 * j + 16 * pp + 8 * h) * 2;
+          __builtin_amdgcn_raw_buffer_store_b128(
+              __builtin_bit_cast(decltype(__builtin_amdgcn_raw_buffer_load_b128(rc, 0, 0, 0)), v),
+              rc, o, 0, 0);
+        }
+      }
+    }
+  };
+  uint4 a0[CH], a1[CH];
+  load_strip(a0, q0);
+  for (int64_t q = q0; q < strips; q += 2 * stride) {
+    run_strip(a0, a1, q);
+    if (q + stride >= strips) break;
+    run_strip(a1, a0, q + stride);
   }
 }
 
@@ -448,10 +665,58 @@ static void launch_rows(const RowsGemm &g, dim3 grid, hipStream_t st) {
   }
 }
 
+// resident workgroups that fit on one CU (registers and LDS), from the runtime
+template <typename T, int D, bool RESID, int NZ>
+static int resident_per_cu() {
+  static int per_cu = 0;
+  if (per_cu == 0) {
+    int nb = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, k_rows_resident<T, D, RESID, NZ>,
+                                                     RR_THREADS, 0) != hipSuccess || nb < 1)
+      nb = 1;
+    per_cu = nb;
+  }
+  return per_cu;
+}
+
+template <typename T, int D, bool RESID, int NZ>
+static void launch_resident_k(const RowsGemm &g, hipStream_t st) {
+  // workgroups per (XCD, output split): fill the CUs of the XCD (32 each),
+  // but no more than the strips need
+  const int nsplit = NZ == 1 ? g.nout : 1;
+  const int64_t strips = cdiv(g.n, 32);
+  int64_t groups = std::max<int64_t>(1, (int64_t)resident_per_cu<T, D, RESID, NZ>() * 32 / nsplit);
+  groups = std::max<int64_t>(1, std::min<int64_t>(groups, cdiv(strips, 8 * RR_WAVES)));
+  const dim3 grid((unsigned)(8 * groups * nsplit));
+  k_rows_resident<T, D, RESID, NZ><<<grid, RR_THREADS, 0, st>>>(g, (int)groups);
+}
+
+// all three Q/K/V weights stay in LDS together where they fit (128 KB), so
+// each strip of X is read once; otherwise workgroups split the outputs
+template <typename T, int D>
+static void launch_resident(const RowsGemm &g, hipStream_t st) {
+  constexpr bool three_fit = 3 * D * D * (int)sizeof(T) <= 128 * 1024;
+  if (g.R) launch_resident_k<T, D, true, 1>(g, st);
+  else if (g.nout == 3 && three_fit) launch_resident_k<T, D, false, three_fit ? 3 : 1>(g, st);
+  else launch_resident_k<T, D, false, 1>(g, st);
+}
+
 // transb = false: one source (NA = 1); transb = true: four (NA = 4)
 gt_status launch_rows_gemm(gt_dtype dt, RowsGemm g, int nout, bool transb, hipStream_t st) {
   if (g.n == 0) return GT_OK;
   g.nout = nout;
+  if (!transb && !(dt == GT_F32 && g.d == 256)) {
+    if (dt == GT_F32) {
+      if (g.d == 64) launch_resident<float, 64>(g, st);
+      else launch_resident<float, 128>(g, st);
+    } else {
+      if (g.d == 64) launch_resident<bf16_t, 64>(g, st);
+      else if (g.d == 128) launch_resident<bf16_t, 128>(g, st);
+      else launch_resident<bf16_t, 256>(g, st);
+    }
+    GT_CHECK_LAUNCH();
+    return GT_OK;
+  }
   const dim3 grid((unsigned)cdiv(g.n, RG_ROWS));
   if (dt == GT_F32) {
     if (transb) launch_rows<float, true, 4>(g, grid, st);
