@@ -57,12 +57,14 @@ def byte_model(cfg, R, M, E, M_nz):
 
 # the sources that decide what the kernels read and write: the kernels, their
 # device helpers and layouts, and the schedule they run over
-KERNEL_SOURCES = ["attn.hip", "device.hpp", "layout.hpp", "prep.hip", "proj.hip"]
+KERNEL_SOURCES = ["attn.hip", "device.hpp", "layout.hpp", "prep.hip"]
+# the dense projection kernels of the layer and what they include
+PROJ_SOURCES = ["proj.hip", "device.hpp"]
 
 
-def kernel_source_hash() -> str:
+def kernel_source_hash(kernel: str = "") -> str:
     h = hashlib.sha256()
-    for f in KERNEL_SOURCES:
+    for f in (PROJ_SOURCES if kernel.startswith("proj") else KERNEL_SOURCES):
         with open(os.path.join(CSRC, f), "rb") as fh:
             h.update(f.encode() + b"\0" + fh.read())
     return h.hexdigest()[:16]
@@ -79,7 +81,7 @@ def traffic_record(kernel: str, workload: str):
         m = re.match(r"^([a-z_]+):\s*(\S+)", line.strip())
         if m:
             rec[m.group(1)] = m.group(2)
-    if rec.get("source_hash") != kernel_source_hash():
+    if rec.get("source_hash") != kernel_source_hash(kernel):
         return None
     try:
         return float(rec["hbm_bytes_per_launch"])
@@ -406,7 +408,9 @@ def layer_bench(args, cfg):
         "value": E / (ms_step * 1e-3) / 1e9,
         "unit": "GEdges/s",
         "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms_step,
-        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        # the projections multiply in the storage type (fp32 accumulation)
+        "dtype": cfg.dtype,
         "data": "synthetic (seeded generators standing in for the pages' graphs)",
         "config": {"workload": f"{cfg.name} layer: {cfg.desc}", "nodes": n, "nnz": E,
                    "heads": H, "head_dim": dh, "d": d, "storage": cfg.dtype,
