@@ -145,6 +145,10 @@ def main():
     ap.add_argument("--layer", action="store_true",
                     help="time a whole layer (dense projections + attention, fwd+bwd) "
                          "instead of the attention alone")
+    ap.add_argument("--head-split", type=int, default=0, metavar="P",
+                    help="time the head repack of graph parallelism with all-to-all for P "
+                         "workers (split of Q, K, V and merge of Y) and the attention run on "
+                         "the P head slices, instead of the plain attention step")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
                     help="only run a plain device-to-device copy of MIB MiB, 5 times "
                          "(calibrates the HBM byte counters against a known size)")
@@ -173,6 +177,8 @@ def main():
     cfg = I.CONFIGS[args.config]
     if args.layer:
         return layer_bench(args, cfg)
+    if args.head_split:
+        return head_split_bench(args, cfg)
     t0 = time.perf_counter()
     P = I.make_problem(cfg)
     gen_s = time.perf_counter() - t0
@@ -423,6 +429,82 @@ def layer_bench(args, cfg):
                    "kernel_source_hash": kernel_source_hash()},
     }
     print(json.dumps(line), flush=True)
+
+
+def head_split_bench(args, cfg):
+    """Graph parallelism with all-to-all, its on-GPU part with the P workers
+    on one GPU: split Q, K, V (and the bias) into P head slices, attention
+    fwd+bwd on each slice over the whole graph, merge Y, lse and the
+    gradients.  The repack kernels are pure copies: `roofline` is theirs
+    (2 R D s bytes per split or merge of a [R, H, dh] tensor)."""
+    import torch
+
+    from graph_transformer_sparse_amd import gtattn as T
+    from graph_transformer_sparse_amd import inputs as I
+
+    parts = args.head_split
+    if cfg.heads % parts:
+        print(f"{cfg.heads} heads do not divide among {parts} workers", file=sys.stderr)
+        sys.exit(2)
+    P = I.make_problem(cfg)
+    dev = torch.device("cuda:0")
+    tdt = torch.float32 if cfg.dtype == "f32" else torch.bfloat16
+    put = lambda x, dt: torch.from_numpy(np.ascontiguousarray(x)).to(dt).to(dev).contiguous()
+    g = T.gt_graph_prepare(put(P.indptr, torch.int32), put(P.indices, torch.int32), cfg.n_cols)
+    Q, K, V, dY = (put(x, tdt) for x in (P.Q, P.K, P.V, P.dY))
+    bias = put(P.bias, torch.float32) if P.bias is not None else None
+    R, H, dh = Q.shape
+    s = Q.element_size()
+
+    def step():
+        return T.attn_head_sliced(g, Q, K, V, dY, bias, P.scale, parts)
+
+    # the repack alone: split of Q into a preallocated buffer, merge back
+    qs = T.gt_head_split(Q, parts)
+    qm = torch.empty_like(Q)
+    ev = lambda: torch.cuda.Event(enable_timing=True)
+    for _ in range(args.warmup):
+        T.gt_head_split(Q, parts, out=qs)
+        T.gt_head_merge(qs, out=qm)
+        step()
+    torch.cuda.synchronize()
+    reps = max(args.steps, 10)
+    a, b, c = ev(), ev(), ev()
+    a.record()
+    for _ in range(reps):
+        T.gt_head_split(Q, parts, out=qs)
+    b.record()
+    for _ in range(reps):
+        T.gt_head_merge(qs, out=qm)
+    c.record()
+    torch.cuda.synchronize()
+    assert torch.equal(qm, Q)
+    nbytes = 2 * R * H * dh * s
+    split_ms, merge_ms = a.elapsed_time(b) / reps, b.elapsed_time(c) / reps
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    ms_step = (time.perf_counter() - t0) * 1e3 / args.steps
+    ach = nbytes / (split_ms * 1e-3) / 1e9
+    print(json.dumps({
+        "metric": f"GEdges/s sparse graph attention fwd+bwd on {parts} head slices "
+                  "(repack + per-slice attention), 1 MI355X",
+        "value": P.nnz / (ms_step * 1e-3) / 1e9, "unit": "GEdges/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms_step,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
+        "data": "synthetic (seeded generators standing in for the pages' graphs)",
+        "config": {"workload": f"{cfg.name}: {cfg.desc}", "parts": parts, "nodes": R,
+                   "heads": H, "head_dim": dh, "storage": cfg.dtype, "bias": cfg.bias,
+                   "parallelism": "single GPU (the P workers' head slices in turn)"},
+        "roofline": {"bound": "hbm", "kernel": "head_split", "achieved": ach,
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": ach / HBM_PEAK_GBS,
+                     "traffic": None},
+        "cpu_baseline": None,
+        "detail": {"head_split_ms": split_ms, "head_merge_ms": merge_ms,
+                   "head_merge_GBps": nbytes / (merge_ms * 1e-3) / 1e9,
+                   "bytes_per_repack": nbytes},
+    }), flush=True)
 
 
 if __name__ == "__main__":

@@ -19,7 +19,7 @@ INCLUDE = os.path.join(os.path.dirname(HERE), "include")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 
-SOURCES = ["prep.hip", "attn.hip", "api.hip", "proj.hip"]
+SOURCES = ["prep.hip", "attn.hip", "api.hip", "proj.hip", "heads.hip"]
 
 FLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-Wall",

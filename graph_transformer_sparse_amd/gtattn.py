@@ -12,6 +12,7 @@ autograd wrapper GTAttnFn / sparse_graph_attention.
 from __future__ import annotations
 
 import ctypes as C
+import math
 import os
 import re
 
@@ -85,6 +86,8 @@ def lib():
         "gt_prof_enable": (_i32, [_i32]),
         "gt_prof_reset": (_i32, []),
         "gt_prof_query": (_i32, [C.c_char_p, C.POINTER(C.c_double), C.POINTER(_i64)]),
+        "gt_head_split": (_i32, [_i64, _i32, _i32, _i32, _P, _P, _P]),
+        "gt_head_merge": (_i32, [_i64, _i32, _i32, _i32, _P, _P, _P]),
         "gt_status_str": (C.c_char_p, [_i32]),
         "gt_last_error": (C.c_char_p, []),
         "gt_version": (_i32, []),
@@ -414,3 +417,69 @@ class SGALayerFn(torch.autograd.Function):
 
 def sga_layer(g: Graph, heads: int, X, Wq, Wk, Wv, Wo, bias=None, scale=None):
     return SGALayerFn.apply(g, heads, X, Wq, Wk, Wv, Wo, bias, scale)
+
+
+# ----------------------------------------------------------------------------
+# head repack of graph parallelism with all-to-all (include/gt_heads.h)
+# ----------------------------------------------------------------------------
+
+def _heads_geometry(t: torch.Tensor):
+    """(rows, heads, head_bytes) of a contiguous [rows, heads, ...] tensor."""
+    assert t.is_contiguous() and t.dim() >= 2
+    rows, heads = t.shape[0], t.shape[1]
+    per_head = t[0, 0].numel() if rows > 0 else math.prod(t.shape[2:])
+    return rows, heads, int(per_head) * t.element_size()
+
+
+def gt_head_split(x: torch.Tensor, parts: int, out=None) -> torch.Tensor:
+    """[rows, heads, ...] -> [parts, rows, heads/parts, ...]: part r holds
+    heads r*heads/parts .. (r+1)*heads/parts - 1 of every row."""
+    rows, heads, hb = _heads_geometry(x)
+    shape = (parts, rows, heads // parts) + tuple(x.shape[2:])
+    out = torch.empty(shape, dtype=x.dtype, device=x.device) if out is None else out
+    _check(lib().gt_head_split(rows, heads, hb, parts, _ptr(x), _ptr(out), _stream(x.device)),
+           "gt_head_split")
+    return out
+
+
+def gt_head_merge(p: torch.Tensor, out=None) -> torch.Tensor:
+    """The inverse of gt_head_split: [parts, rows, hp, ...] -> [rows, parts*hp, ...]."""
+    assert p.is_contiguous() and p.dim() >= 3
+    parts, rows, hp = p.shape[0], p.shape[1], p.shape[2]
+    heads = parts * hp
+    hb = math.prod(p.shape[3:]) * p.element_size()
+    shape = (rows, heads) + tuple(p.shape[3:])
+    out = torch.empty(shape, dtype=p.dtype, device=p.device) if out is None else out
+    _check(lib().gt_head_merge(rows, heads, hb, parts, _ptr(p), _ptr(out), _stream(p.device)),
+           "gt_head_merge")
+    return out
+
+
+def attn_head_sliced(g: Graph, Q, K, V, dY=None, bias=None, scale=None, parts: int = 2):
+    """The attention as graph parallelism with all-to-all computes it, with
+    the `parts` workers on one GPU: the heads are split into `parts` slices
+    (what each worker holds after the first all-to-all), the attention runs
+    on each slice over the whole graph, and the outputs are merged back
+    (the return all-to-all).  Returns (Y, lse) and, with dY, also
+    (dQ, dK, dV, dbias)."""
+    R, H, dh = Q.shape
+    scale = dh ** -0.5 if scale is None else float(scale)
+    q, k, v = (gt_head_split(t, parts) for t in (Q, K, V))
+    b = gt_head_split(bias, parts) if bias is not None else None
+    br = lambda r: b[r] if b is not None else None
+    # per-slice outputs go straight into the packed layout the merge reads
+    Yp = torch.empty_like(q)
+    lsep = torch.empty((parts, R, H // parts), dtype=torch.float32, device=Q.device)
+    for r in range(parts):
+        gt_attn_fwd(g, q[r], k[r], v[r], br(r), scale, Y=Yp[r], lse=lsep[r])
+    Y, lse = gt_head_merge(Yp), gt_head_merge(lsep)
+    if dY is None:
+        return Y, lse
+    dy = gt_head_split(dY, parts)
+    dQp, dKp, dVp = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    dBp = torch.empty_like(b) if b is not None else None
+    for r in range(parts):
+        gt_attn_bwd(g, q[r], k[r], v[r], lsep[r], dy[r], br(r), scale, dQ=dQp[r], dK=dKp[r],
+                    dV=dVp[r], dbias=dBp[r] if dBp is not None else None)
+    dB = gt_head_merge(dBp) if dBp is not None else None
+    return Y, lse, gt_head_merge(dQp), gt_head_merge(dKp), gt_head_merge(dVp), dB

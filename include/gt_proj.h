@@ -21,7 +21,8 @@
  * act as X W; weight gradients dW_* are [d, d] float32.  d in {64, 128, 256}.
  * The products run on the matrix cores with float32 accumulation; bf16
  * outputs are rounded to nearest even.  Results are bitwise deterministic:
- * the weight gradients sum fixed chunks of 8192 node rows in chunk order.
+ * the weight gradients sum per-slot partial products (slots of contiguous
+ * node rows, a function of n and d only) in slot order.
  * Errors: GT_E_NULL, GT_E_ALIGN, GT_E_DTYPE, GT_E_SHAPE (d), GT_E_ARG (n),
  * GT_E_WORKSPACE, GT_E_HIP.
  */
@@ -50,7 +51,7 @@ gt_status gt_proj_bwd_data(int64_t n, int32_t d, gt_dtype dt, const void *dZ, co
                            const void *dK, const void *dV, const void *Wo, const void *Wq,
                            const void *Wk, const void *Wv, void *dX, void *stream);
 
-/* Bytes of `work` gt_proj_bwd_weight needs (per-chunk partial products). */
+/* Bytes of `work` gt_proj_bwd_weight needs (per-slot partial products). */
 size_t gt_proj_work_bytes(int64_t n, int32_t d);
 
 /* dW_o = X^T dZ, dW_Q = X^T dQ, dW_K = X^T dK, dW_V = X^T dV (float32). */

@@ -148,6 +148,17 @@ def test_proj_argument_checks(L):
     assert L.gt_proj_out(10, 128, 1, FAKE, ODD, FAKE, FAKE, None) == 5
     assert L.gt_proj_out(-1, 128, 1, FAKE, FAKE, FAKE, FAKE, None) == 2
     nb = L.gt_proj_work_bytes(100000, 128)
-    assert nb >= 4 * 13 * 128 * 128 * 4          # 13 chunks of 8192 rows, 4 gradients
+    assert nb >= 4 * 128 * 128 * 128 * 4         # 128 row slots, 4 gradients of [128, 128]
     assert L.gt_proj_bwd_weight(100000, 128, 0, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
                                 FAKE, FAKE, nb - 1, None) == 7
+
+
+def test_heads_argument_checks(L):
+    # rows, heads, head_bytes, parts, src, dst, stream
+    assert L.gt_head_split(10, 6, 64, 4, FAKE, FAKE, None) == 4     # heads % parts
+    assert L.gt_head_split(10, 8, 6, 2, FAKE, FAKE, None) == 4      # head_bytes not a multiple of 4
+    assert L.gt_head_split(10, 8, 64, 0, FAKE, FAKE, None) == 2     # parts
+    assert L.gt_head_merge(-1, 8, 64, 2, FAKE, FAKE, None) == 2     # rows
+    assert L.gt_head_merge(10, 8, 64, 2, None, FAKE, None) == 1
+    assert L.gt_head_split(10, 8, 64, 2, FAKE, C.c_void_p(0x20000002), None) == 5  # alignment
+    assert L.gt_head_split(0, 8, 64, 2, None, None, None) == 0      # nothing to move
