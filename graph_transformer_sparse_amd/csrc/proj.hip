@@ -493,8 +493,9 @@ __global__ __launch_bounds__(RR_THREADS) void k_rows_resident(RowsGemm g, int gr
 // part[s][slot], and a second kernel sums the slots in slot order
 // (deterministic, no atomics).  Per step a workgroup stages KT = 32 rows
 // of X and G_s into LDS transposed to [column][row] (two rows per thread,
-// swapped into column pairs in registers), the next step's rows already in
-// flight, and its wavefronts each multiply a (32 MB) x (32 NB) block.
+// swapped into column pairs in registers), the rows of the next PD steps
+// already in flight, and its wavefronts each multiply a (32 MB) x (32 NB)
+// block.
 // Workgroups of one slot sit eight block indices apart, so the four that
 // share X rows land on the same XCD (and L2).
 // ---------------------------------------------------------------------------
@@ -533,6 +534,7 @@ void k_gemm_wgrad(WgradGemm g) {
   constexpr int CH = WG_KT / (2 * AV);          // k ranges per step
   constexpr int UOP = (WG_KT / 2) * (D / AV);   // row-pair units per operand
   constexpr int SU = (2 * UOP + NT - 1) / NT;   // units per thread
+  static_assert(UOP % WAVE == 0 && 2 * UOP == SU * NT, "staging units fill the workgroup");
   constexpr int TILE = D * WG_KT;
   __shared__ __align__(16) T Xs[TILE];
   __shared__ __align__(16) T Gs[TILE];
@@ -545,7 +547,12 @@ void k_gemm_wgrad(WgradGemm g) {
   const int64_t r1 = std::min<int64_t>(r0 + g.rows_per_slot, g.n);
   const T *X = (const T *)g.X, *G = (const T *)g.G[s];
 
-  uint4 st[2 * SU];
+  // staging registers of the next PD steps (a ring, indexed statically by
+  // unrolling the step loop PD times); rows go through a buffer resource
+  // bounded to the step's rows of the slot, so rows past the slot read as 0
+  constexpr int PD = (D == 256 && sizeof(T) == 4) ? 1 : (D == 256 ? 2 : 4);
+  constexpr int RB = D * (int)sizeof(T);
+  uint4 st[PD][2 * SU];
   // unit u: operand u / UOP, column group mg, row pair kp of the step
   auto unit = [&](int u, int &op, int &mg, int &kp) {
     const int v = u % UOP;
@@ -554,20 +561,25 @@ void k_gemm_wgrad(WgradGemm g) {
     mg = rest % (D / AV);
     kp = lo + 4 * (rest / (D / AV));
   };
-  auto fetch = [&](int64_t k0) {
+  auto fetch = [&](uint4 (&dst)[2 * SU], int64_t k0) {
+    const int64_t nrow = k0 < r1 ? std::min<int64_t>(WG_KT, r1 - k0) : 0;
+    const int64_t kb = k0 < r1 ? k0 : 0;
+    const auto rx = __builtin_amdgcn_make_buffer_rsrc((void *)(X + kb * D), 0, (int)(nrow * RB), BUF_WORD3);
+    const auto rg = __builtin_amdgcn_make_buffer_rsrc((void *)(G + kb * D), 0, (int)(nrow * RB), BUF_WORD3);
 #pragma unroll
     for (int i = 0; i < SU; ++i) {
       const int u = tid + i * NT;
       int op, mg, kp;
       unit(u, op, mg, kp);
-      const T *P = op == 0 ? X : G;
-      const int64_t row = k0 + 2 * kp;
-      const bool ok = u < 2 * UOP;
-      st[2 * i] = load16(P + row * D + mg * AV, ok && row < r1);
-      st[2 * i + 1] = load16(P + (row + 1) * D + mg * AV, ok && row + 1 < r1);
+      // UOP is a multiple of 64, so the operand is the same for a whole
+      // wavefront: pick its buffer resource in scalar registers
+      const auto r = __builtin_amdgcn_readfirstlane(op) == 0 ? rx : rg;
+      const int o = 2 * kp * RB + mg * 16;
+      dst[2 * i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, o, 0, 0));
+      dst[2 * i + 1] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, o + RB, 0, 0));
     }
   };
-  auto put = [&]() {
+  auto put = [&](const uint4 (&src)[2 * SU]) {
 #pragma unroll
     for (int i = 0; i < SU; ++i) {
       const int u = tid + i * NT;
@@ -578,7 +590,7 @@ void k_gemm_wgrad(WgradGemm g) {
         int off[AV];
 #pragma unroll
         for (int c = 0; c < AV; ++c) off[c] = wtile_off<T>(mg * AV + c, k / AV) + k % AV;
-        store_pair_t<T>(op == 0 ? Xs : Gs, st[2 * i], st[2 * i + 1], off);
+        store_pair_t<T>(op == 0 ? Xs : Gs, src[2 * i], src[2 * i + 1], off);
       }
     }
   };
@@ -591,27 +603,34 @@ void k_gemm_wgrad(WgradGemm g) {
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
 
-  if (r0 < r1) fetch(r0);
-  for (int64_t k0 = r0; k0 < r1; k0 += WG_KT) {
-    __syncthreads();
-    put();
-    __syncthreads();
-    if (k0 + WG_KT < r1) fetch(k0 + WG_KT);
+  // steps of WG_KT rows, padded to a multiple of PD (the padding steps read
+  // zeros and add nothing)
+  const int64_t nsteps = r0 < r1 ? (r1 - r0 + WG_KT - 1) / WG_KT : 0;
 #pragma unroll
-    for (int c = 0; c < CH; ++c) {
-      uint4 av[S::MB], bv[S::NB];
+  for (int q = 0; q < PD; ++q) fetch(st[q], r0 + (int64_t)q * WG_KT);
+  for (int64_t i0 = 0; i0 < nsteps; i0 += PD) {
 #pragma unroll
-      for (int i = 0; i < S::MB; ++i)
-        av[i] = *reinterpret_cast<const uint4 *>(
-            Xs + wtile_off<T>(32 * (wm * S::MB + i) + lane % 32, 2 * c + h));
+    for (int q = 0; q < PD; ++q) {
+      __syncthreads();
+      put(st[q]);
+      __syncthreads();
+      fetch(st[q], r0 + (i0 + q + PD) * WG_KT);
 #pragma unroll
-      for (int j = 0; j < S::NB; ++j)
-        bv[j] = *reinterpret_cast<const uint4 *>(
-            Gs + wtile_off<T>(32 * (wn * S::NB + j) + lane % 32, 2 * c + h));
+      for (int c = 0; c < CH; ++c) {
+        uint4 av[S::MB], bv[S::NB];
 #pragma unroll
-      for (int i = 0; i < S::MB; ++i)
+        for (int i = 0; i < S::MB; ++i)
+          av[i] = *reinterpret_cast<const uint4 *>(
+              Xs + wtile_off<T>(32 * (wm * S::MB + i) + lane % 32, 2 * c + h));
 #pragma unroll
-        for (int j = 0; j < S::NB; ++j) acc[i][j] = M::mma(av[i], bv[j], acc[i][j]);
+        for (int j = 0; j < S::NB; ++j)
+          bv[j] = *reinterpret_cast<const uint4 *>(
+              Gs + wtile_off<T>(32 * (wn * S::NB + j) + lane % 32, 2 * c + h));
+#pragma unroll
+        for (int i = 0; i < S::MB; ++i)
+#pragma unroll
+          for (int j = 0; j < S::NB; ++j) acc[i][j] = M::mma(av[i], bv[j], acc[i][j]);
+      }
     }
   }
   float *P = g.part + ((int64_t)s * g.slots + slot) * D * D;
