@@ -487,6 +487,158 @@ __global__ __launch_bounds__(RR_THREADS) void k_rows_resident(RowsGemm g, int gr
 }
 
 // ---------------------------------------------------------------------------
+// four-source row GEMM (the input gradient): C = sum_s A_s W_s^T, D <= 128.
+//
+// Each wavefront owns a 32-row strip and keeps the whole [32, D] result in
+// registers (J accumulator blocks) while the k dimension streams through in
+// slabs of NCS 16-byte chunks: for each source s and slab, the workgroup
+// stages rows n of W_s restricted to the slab's k (contiguous in W_s, since
+// B_s = W_s^T) into LDS, double-buffered with one barrier per slab, and each
+// wavefront multiplies its strip's chunks of A_s by them.  A chunk of the
+// strip is dead once its slab is done, so its register is refilled at once
+// with the same chunk of the next source (or of the next strip's first
+// source): the A loads run one source ahead without extra registers, and
+// they are issued before the strip's stores, so waiting for them never waits
+// for a store (the memory counter is in order).  Workgroups are persistent
+// over 256-row strips; all global accesses go through bounded buffer
+// resources (no branches at the ragged end).
+// ---------------------------------------------------------------------------
+constexpr int S4_WAVES = 8, S4_THREADS = S4_WAVES * WAVE;
+constexpr int S4_ROWS = S4_WAVES * 32;
+constexpr int S4_NCS = 2;                          // 16-byte chunks (k) per slab
+constexpr int S4_PITCH = S4_NCS * 32 + 16;         // LDS bytes per weight row of a slab
+
+// the four outputs of block j of a lane (row lane % 32), as stored
+template <typename T>
+__device__ inline void store_strip_block(__amdgpu_buffer_rsrc_t rc, int RB, int j, int lane,
+                                         const v16f &acc) {
+  const int h = lane / 32, m = lane % 32;
+  if constexpr (sizeof(T) == 4) {
+#pragma unroll
+    for (int gq = 0; gq < 4; ++gq) {
+      const uint4 v = make_uint4(__float_as_uint(acc[4 * gq]), __float_as_uint(acc[4 * gq + 1]),
+                                 __float_as_uint(acc[4 * gq + 2]), __float_as_uint(acc[4 * gq + 3]));
+      __builtin_amdgcn_raw_buffer_store_b128(
+          __builtin_bit_cast(decltype(__builtin_amdgcn_raw_buffer_load_b128(rc, 0, 0, 0)), v), rc,
+          m * RB + (32 * j + 8 * gq + 4 * h) * 4, 0, 0);
+    }
+  } else {
+    uint2 pk[4];
+#pragma unroll
+    for (int gq = 0; gq < 4; ++gq)
+      pk[gq] = make_uint2(bf16_rne(acc[4 * gq]) | (bf16_rne(acc[4 * gq + 1]) << 16),
+                          bf16_rne(acc[4 * gq + 2]) | (bf16_rne(acc[4 * gq + 3]) << 16));
+#pragma unroll
+    for (int pp = 0; pp < 2; ++pp) {
+      const uint2 mine = h ? pk[2 * pp + 1] : pk[2 * pp];
+      const uint2 give = h ? pk[2 * pp] : pk[2 * pp + 1];
+      const uint2 got = make_uint2((uint32_t)__shfl_xor((int)give.x, 32),
+                                   (uint32_t)__shfl_xor((int)give.y, 32));
+      const uint4 v = h ? make_uint4(got.x, got.y, mine.x, mine.y)
+                        : make_uint4(mine.x, mine.y, got.x, got.y);
+      __builtin_amdgcn_raw_buffer_store_b128(
+          __builtin_bit_cast(decltype(__builtin_amdgcn_raw_buffer_load_b128(rc, 0, 0, 0)), v), rc,
+          m * RB + (32 * j + 16 * pp + 8 * h) * 2, 0, 0);
+    }
+  }
+}
+
+template <typename T, int D>
+__global__ __launch_bounds__(S4_THREADS) void k_rows_sum4(RowsGemm g) {
+  using M = Mma<T>;
+  constexpr int AV = 16 / sizeof(T), CH = D / (2 * AV), RB = D * (int)sizeof(T);
+  constexpr int JW = D / 32;                              // column blocks
+  static_assert(D <= 128, "a strip and its result must fit one wavefront's registers");
+  constexpr int NSLAB = CH / S4_NCS;                      // slabs per source
+  constexpr int SV = D * 2 * S4_NCS;                      // 16-byte vectors per slab
+  constexpr int SU = (SV + S4_THREADS - 1) / S4_THREADS;  // per thread
+  static_assert(CH % S4_NCS == 0 && NSLAB % 2 == 0, "slab parity");
+  __shared__ __align__(16) char Bs[2][D * S4_PITCH];
+  const int tid = threadIdx.x, lane = tid & (WAVE - 1), h = lane / 32;
+  const int w = __builtin_amdgcn_readfirstlane(tid / WAVE);
+  const int64_t nblk = (g.n + S4_ROWS - 1) / S4_ROWS;
+  const int64_t first = blockIdx.x, stride = gridDim.x;
+  const int aoff = (lane % 32) * RB + h * 16;
+
+  // weight slab (source s, slab c0): row n, vectors 0 .. 2 NCS - 1
+  uint4 sv[SU];
+  // a lane's byte offset in W_s of its staging vectors (the slab adds a
+  // uniform offset); buffer loads keep the per-source bases in scalars
+  int woff[SU];
+#pragma unroll
+  for (int i = 0; i < SU; ++i) {
+    const int u = (tid + i * S4_THREADS) % SV;       // every thread loads (duplicates unused)
+    woff[i] = (u / (2 * S4_NCS)) * RB + (u % (2 * S4_NCS)) * 16;
+  }
+  auto fetch_w = [&](int s, int slab) {
+    const auto rw = __builtin_amdgcn_make_buffer_rsrc((void *)g.B[0][s], 0, D * RB, BUF_WORD3);
+#pragma unroll
+    for (int i = 0; i < SU; ++i)
+      sv[i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rw, woff[i], slab * S4_NCS * 32, 0));
+  };
+  auto put_w = [&](char *buf) {
+#pragma unroll
+    for (int i = 0; i < SU; ++i) {
+      const int u = tid + i * S4_THREADS;
+      if (u < SV) {
+        const int n = u / (2 * S4_NCS), v = u % (2 * S4_NCS);
+        *reinterpret_cast<uint4 *>(buf + n * S4_PITCH + v * 16) = sv[i];
+      }
+    }
+  };
+  auto strip_of = [&](int64_t blk) { return (blk * S4_WAVES + w) * 32; };   // first row
+
+  uint4 a[CH];
+  {
+    const auto ra = strip_rsrc(g.A[0], strip_of(first), g.n, RB);
+#pragma unroll
+    for (int c = 0; c < CH; ++c)
+      a[c] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(ra, aoff + 32 * c, 0, 0));
+  }
+  fetch_w(0, 0);
+  put_w(Bs[0]);
+  for (int64_t blk = first; blk < nblk; blk += stride) {
+    const int64_t row0 = strip_of(blk);
+    v16f acc[JW];
+#pragma unroll
+    for (int j = 0; j < JW; ++j)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[j][v] = 0.f;
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      // where the chunks freed in this source go: the next source of this
+      // strip, or the first source of the next strip
+      const auto rn = s < 3 ? strip_rsrc(g.A[s + 1], row0, g.n, RB)
+                            : strip_rsrc(g.A[0], strip_of(blk + stride), g.n, RB);
+#pragma unroll
+      for (int slab = 0; slab < NSLAB; ++slab) {
+        __syncthreads();                       // Bs[slab & 1] is complete
+        // the next slab's weights (the first slab of source 0 after the last)
+        if (slab + 1 < NSLAB) fetch_w(s, slab + 1);
+        else fetch_w(s < 3 ? s + 1 : 0, 0);
+        const char *buf = Bs[slab & 1];
+#pragma unroll
+        for (int cc = 0; cc < S4_NCS; ++cc) {
+          const int c = slab * S4_NCS + cc;
+          asm volatile("" ::: "memory");       // one chunk's weight reads at a time
+#pragma unroll
+          for (int j = 0; j < JW; ++j) {
+            const uint4 wv = *reinterpret_cast<const uint4 *>(
+                buf + (32 * j + lane % 32) * S4_PITCH + (2 * cc + h) * 16);
+            acc[j] = M::mma(wv, a[c], acc[j]);
+          }
+          a[c] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rn, aoff + 32 * c, 0, 0));
+        }
+        put_w(Bs[(slab + 1) & 1]);
+      }
+    }
+    const auto rc = strip_rsrc(g.C[0], row0, g.n, RB);
+#pragma unroll
+    for (int j = 0; j < JW; ++j) store_strip_block<T>(rc, RB, j, lane, acc[j]);
+  }
+}
+
+// ---------------------------------------------------------------------------
 // weight gradient: dW_s = X^T G_s, a contraction over the n node rows.
 // The rows are cut into `slots` contiguous ranges; workgroup (s, slot)
 // computes the whole [D, D] product of its range for gradient s into
@@ -721,9 +873,37 @@ static void launch_resident(const RowsGemm &g, hipStream_t st) {
 }
 
 // transb = false: one source (NA = 1); transb = true: four (NA = 4)
+template <typename T, int D>
+static void launch_sum4(const RowsGemm &g, hipStream_t st) {
+  static int per_cu = 0;
+  if (per_cu == 0) {
+    int nb = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, k_rows_sum4<T, D>, S4_THREADS, 0) !=
+            hipSuccess || nb < 1)
+      nb = 1;
+    per_cu = nb;
+  }
+  const int64_t nblk = cdiv(g.n, S4_ROWS);
+  const int64_t grid = std::min<int64_t>(nblk, (int64_t)per_cu * 256);
+  k_rows_sum4<T, D><<<dim3((unsigned)grid), S4_THREADS, 0, st>>>(g);
+}
+
 gt_status launch_rows_gemm(gt_dtype dt, RowsGemm g, int nout, bool transb, hipStream_t st) {
   if (g.n == 0) return GT_OK;
   g.nout = nout;
+  if (transb && g.d <= 128) {   // the input gradient: four sources
+    // (at d = 256 the column-tiled kernel below measured faster: the slab
+    // kernel must split a strip over two wavefronts there)
+    if (dt == GT_F32) {
+      if (g.d == 64) launch_sum4<float, 64>(g, st);
+      else launch_sum4<float, 128>(g, st);
+    } else {
+      if (g.d == 64) launch_sum4<bf16_t, 64>(g, st);
+      else launch_sum4<bf16_t, 128>(g, st);
+    }
+    GT_CHECK_LAUNCH();
+    return GT_OK;
+  }
   if (!transb && !(dt == GT_F32 && g.d == 256)) {
     if (dt == GT_F32) {
       if (g.d == 64) launch_resident<float, 64>(g, st);
