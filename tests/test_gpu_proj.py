@@ -15,6 +15,7 @@ import torch
 from graph_transformer_sparse_amd import gtattn as T
 from graph_transformer_sparse_amd import inputs as I
 from oracle import layer as L
+from oracle import oracle as O
 
 from gpu_util import RTOL, TDT, assert_close, dev, to_np
 
@@ -109,3 +110,43 @@ def test_empty_node_set():
     assert dX.shape == (0, d)
     for dw in T.gt_proj_bwd_weight(X, X, X, X, X):
         assert dw.shape == (d, d) and torch.count_nonzero(dw).item() == 0
+
+
+def test_layer_at_mid_size():
+    """The whole layer at the Mid workload's size (131,072 nodes, 1.8M
+    nonzeros, d = 128, fp32), forward and backward, every output against
+    the fp64 oracle.  Magnitudes compose through the layer: a product's is
+    |A| |B| with the attention oracle's magnitudes standing in for |dQ|,
+    |dK|, |dV| and |Y| where those enter."""
+    cfg = I.CONFIGS["mid"]
+    P = I.make_problem(cfg)
+    n, H, dh = cfg.n_rows, cfg.heads, cfg.head_dim
+    d = H * dh
+    X, W, dZ = I.layer_inputs(cfg.idx, n, d, "f32")
+    t = lambda a: dev(a, torch.float32)
+    g = T.gt_graph_prepare(dev(P.indptr), dev(P.indices), n)
+    Xd = t(X).requires_grad_()
+    Wd = {k: t(v).requires_grad_() for k, v in W.items()}
+    print("layer mid: gpu", flush=True)
+    Z = T.sga_layer(g, H, Xd, Wd["q"], Wd["k"], Wd["v"], Wd["o"])
+    Z.backward(t(dZ))
+    torch.cuda.synchronize()
+    print("layer mid: oracle", flush=True)
+    r3 = lambda a: np.asarray(a).reshape(n, H, dh)
+    Q, K, V = L.proj_qkv(X, W["q"], W["k"], W["v"])
+    m = {}
+    Y, _ = O.fwd(P.indptr, P.indices, n, r3(Q), r3(K), r3(V), None, P.scale, mag=m)
+    dQ, dK, dV, _ = O.bwd(P.indptr, P.indices, n, r3(Q), r3(K), r3(V), r3(dZ), None, P.scale, mag=m)
+    f = lambda a: np.asarray(a).reshape(n, d)
+    Y, dQ, dK, dV = f(Y), f(dQ), f(dK), f(dV)
+    mY, mQ, mK, mV = (f(m[k]) for k in ("Y", "dQ", "dK", "dV"))
+    aW = {k: _abs(v) for k, v in W.items()}
+    aX, adZ = _abs(X), _abs(dZ)
+    rt = RTOL["f32"]
+    assert_close(Z, L.proj_out(X, W["o"], Y), rt, "Z", aX @ aW["o"] + mY)
+    rdX = L.proj_bwd_data(dZ, dQ, dK, dV, W["o"], W["q"], W["k"], W["v"])
+    mdX = adZ @ aW["o"].T + mQ @ aW["q"].T + mK @ aW["k"].T + mV @ aW["v"].T
+    assert_close(Xd.grad, rdX, rt, "dX", mdX)
+    rW = L.proj_bwd_weight(X, dZ, dQ, dK, dV)
+    for k, ref, mg in zip("oqkv", rW, (aX.T @ adZ, aX.T @ mQ, aX.T @ mK, aX.T @ mV)):
+        assert_close(Wd[k].grad, ref, rt, "dW" + k, mg)
