@@ -406,9 +406,9 @@ __global__ __launch_bounds__(RR_THREADS) void k_rows_resident(RowsGemm g, int gr
     load_strip(next, q + stride);
     const int64_t row0 = 32 * q;
     const auto rr = strip_rsrc(RESID ? (const void *)R : g.C[0], row0, g.n, RB);
-    // residual of block j, fetched RD blocks ahead (fp32 blocks take twice
-    // the registers, so they look one block ahead instead of two)
-    constexpr int RD = sizeof(T) == 4 ? 1 : 2;
+    // residual of block j, fetched RD blocks ahead (one where registers are
+    // short: fp32 blocks take twice the registers, and D = 256 holds more)
+    constexpr int RD = (sizeof(T) == 4 || D == 256) ? 1 : 2;
     typename O::type rv[RESID ? J : 1][4];
     auto fetch_r = [&](int j) {
 #pragma unroll
@@ -419,6 +419,7 @@ __global__ __launch_bounds__(RR_THREADS) void k_rows_resident(RowsGemm g, int gr
 #pragma unroll
       for (int j = 0; j < RD && j < J; ++j) fetch_r(j);
     }
+    uint4 held[2];                       // bf16: the even block's stores, see below
 #pragma unroll
     for (int t = 0; t < NZ * J; ++t) {
       const int z = t / J, j = t % J;
@@ -435,8 +436,9 @@ __global__ __launch_bounds__(RR_THREADS) void k_rows_resident(RowsGemm g, int gr
       const T *wrow = Ws + (z * D + 32 * j) * D;
 #pragma unroll
       for (int c = 0; c < CH; ++c) {
-        // at most 8 weight vectors in flight per wavefront
-        if (c % 8 == 0 && c > 0) asm volatile("" ::: "memory");
+        // at most 8 (4 at D = 256, where registers are short) weight
+        // vectors in flight per wavefront
+        if (c % (D == 256 ? 4 : 8) == 0 && c > 0) asm volatile("" ::: "memory");
         // chunk 2c + h of row 32 j + m: its low 3 bits are swizzled, the rest
         // is a constant offset
         const uint4 wv = *reinterpret_cast<const uint4 *>(wrow + woff[c % 4] + (c / 4) * 8 * AV);
@@ -461,18 +463,32 @@ __global__ __launch_bounds__(RR_THREADS) void k_rows_resident(RowsGemm g, int gr
           pk[gq] = make_uint2(bf16_rne(x[0]) | (bf16_rne(x[1]) << 16),
                               bf16_rne(x[2]) | (bf16_rne(x[3]) << 16));
         }
+        uint4 v[2];
 #pragma unroll
         for (int pp = 0; pp < 2; ++pp) {
           const uint2 mine = h ? pk[2 * pp + 1] : pk[2 * pp];
           const uint2 give = h ? pk[2 * pp] : pk[2 * pp + 1];
           const uint2 got = make_uint2((uint32_t)__shfl_xor((int)give.x, 32),
                                        (uint32_t)__shfl_xor((int)give.y, 32));
-          const uint4 v = h ? make_uint4(got.x, got.y, mine.x, mine.y)
-                            : make_uint4(mine.x, mine.y, got.x, got.y);
-          const int o = (lane % 32) * RB + (32 * j + 16 * pp + 8 * h) * 2;
-          __builtin_amdgcn_raw_buffer_store_b128(
-              __builtin_bit_cast(decltype(__builtin_amdgcn_raw_buffer_load_b128(rc, 0, 0, 0)), v),
-              rc, o, 0, 0);
+          v[pp] = h ? make_uint4(got.x, got.y, mine.x, mine.y)
+                    : make_uint4(mine.x, mine.y, got.x, got.y);
+        }
+        // a 32-column block is half of a row's 128-byte line: hold an even
+        // block until its odd neighbour is done and write the two together,
+        // so no line leaves L2 half written
+        if (j % 2 == 0) {
+          held[0] = v[0];
+          held[1] = v[1];
+        } else {
+#pragma unroll
+          for (int k = 0; k < 4; ++k) {
+            const int jj = j - 1 + k / 2, pp = k % 2;
+            const uint4 x = k / 2 ? v[pp] : held[pp];
+            const int o = (lane % 32) * RB + (32 * jj + 16 * pp + 8 * h) * 2;
+            __builtin_amdgcn_raw_buffer_store_b128(
+                __builtin_bit_cast(decltype(__builtin_amdgcn_raw_buffer_load_b128(rc, 0, 0, 0)), x),
+                rc, o, 0, 0);
+          }
         }
       }
     }
