@@ -95,3 +95,17 @@ def test_head_sliced_attention(case):
         assert_close(dB, rB, rt, "dbias", head_axis=1)
     else:
         assert dB is None
+
+
+def test_split_at_large_size():
+    """The repack at the Large shape (1,048,576 x 8 x 32 bf16) against the
+    oracle, bit for bit, for every worker count the heads allow."""
+    cfg = I.CONFIGS["large"]
+    n, H, dh = cfg.n_rows, cfg.heads, cfg.head_dim
+    x = torch.from_numpy(np.random.default_rng(3).integers(-2**15, 2**15, (n, H, dh), dtype=np.int16))
+    xd = x.cuda().view(torch.bfloat16)
+    for parts in (2, 4, 8):
+        print(f"heads large parts={parts}", flush=True)
+        s = T.gt_head_split(xd, parts)
+        assert torch.equal(s.view(torch.int16).cpu(), torch.from_numpy(Hd.head_split(x.numpy(), parts)))
+        assert torch.equal(T.gt_head_merge(s).view(torch.int16).cpu(), x)

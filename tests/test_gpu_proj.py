@@ -150,3 +150,38 @@ def test_layer_at_mid_size():
     rW = L.proj_bwd_weight(X, dZ, dQ, dK, dV)
     for k, ref, mg in zip("oqkv", rW, (aX.T @ adZ, aX.T @ mQ, aX.T @ mK, aX.T @ mV)):
         assert_close(Wd[k].grad, ref, rt, "dW" + k, mg)
+
+
+@pytest.mark.parametrize("name", ["large", "hub"])
+def test_projections_at_full_size(name):
+    """The projection kernels at the Large (1,048,576 x 256) and Hub
+    (2,400,000 x 128) node counts in bf16, as the layer benchmark runs them:
+    sampled rows of Q, K, V, Z and dX against the oracle on those rows, and
+    one weight gradient (a sum over every node) in full."""
+    cfg = I.CONFIGS[name]
+    n, d = cfg.n_rows, cfg.heads * cfg.head_dim
+    X, W, dZ = I.layer_inputs(cfg.idx, n, d, "bf16")
+    t = lambda a: dev(a, torch.bfloat16)
+    Xd, dZd, Wd = t(X), t(dZ), {k: t(v) for k, v in W.items()}
+    print(f"projections {name}: gpu", flush=True)
+    Q, K, V = T.gt_proj_qkv(Xd, Wd["q"], Wd["k"], Wd["v"])
+    Z = T.gt_proj_out(Xd, Wd["o"], dZd)                      # dZ stands in for Y
+    dX = T.gt_proj_bwd_data(dZd, Xd, dZd, Xd, Wd["o"], Wd["q"], Wd["k"], Wd["v"])
+    dW = T.gt_proj_bwd_weight(Xd, dZd, Xd, dZd, Xd)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(5)
+    rows = np.unique(np.concatenate([np.arange(64), np.arange(n - 64, n), rng.integers(0, n, 4000)]))
+    idx = torch.from_numpy(rows).cuda()
+    x, z = X[rows], dZ[rows]
+    rt = RTOL["bf16"]
+    print(f"projections {name}: oracle on {rows.size} rows", flush=True)
+    for got, k in zip((Q, K, V), "qkv"):
+        assert_close(got[idx], L.proj_qkv(x, W[k], W[k], W[k])[0], rt, "XW" + k, _abs(x) @ _abs(W[k]))
+    assert_close(Z[idx], L.proj_out(x, W["o"], z), rt, "Z", _abs(x) @ _abs(W["o"]) + _abs(z))
+    rdx = L.proj_bwd_data(z, x, z, x, W["o"], W["q"], W["k"], W["v"])
+    mag = _abs(z) @ _abs(W["o"]).T + _abs(x) @ _abs(W["q"]).T + _abs(z) @ _abs(W["k"]).T + _abs(x) @ _abs(W["v"]).T
+    assert_close(dX[idx], rdx, rt, "dX", mag)
+    print(f"projections {name}: oracle weight gradient", flush=True)
+    Xf, Zf = X.astype(np.float64), dZ.astype(np.float64)
+    assert_close(dW[0], Xf.T @ Zf, 1e-5, "dWo", np.abs(Xf).T @ np.abs(Zf))
+    assert_close(dW[1], Xf.T @ Xf, 1e-5, "dWq", np.abs(Xf).T @ np.abs(Xf))
