@@ -85,7 +85,10 @@ __device__ inline void store_pair_t<float>(float *tile, const uint4 &r0, const u
 
 // ---------------------------------------------------------------------------
 // row GEMM: C_z[rows, :] = sum_s A_s[rows, :] op(W_zs) (+ R), op(W) = W or W^T,
-// every operand [n, D] or [D, D] row-major.
+// every operand [n, D] or [D, D] row-major.  The general, column-tiled form;
+// it serves fp32 at D = 256, where neither the weight (256 KB) fits LDS for
+// the resident kernel nor a strip with its whole result fits the registers
+// for the slab kernel below.
 //
 // A workgroup of 8 wavefronts takes 256 node rows; wavefront w owns rows
 // [32w, 32w + 32) and holds its A strip in registers, loaded straight from
@@ -503,7 +506,8 @@ __global__ __launch_bounds__(RR_THREADS) void k_rows_resident(RowsGemm g, int gr
 }
 
 // ---------------------------------------------------------------------------
-// four-source row GEMM (the input gradient): C = sum_s A_s W_s^T, D <= 128.
+// four-source row GEMM (the input gradient): C = sum_s A_s W_s^T (all but
+// fp32 at D = 256).
 //
 // Each wavefront owns a 32-row strip and keeps the whole [32, D] result in
 // registers (J accumulator blocks) while the k dimension streams through in
@@ -564,7 +568,7 @@ __global__ __launch_bounds__(S4_THREADS) void k_rows_sum4(RowsGemm g) {
   using M = Mma<T>;
   constexpr int AV = 16 / sizeof(T), CH = D / (2 * AV), RB = D * (int)sizeof(T);
   constexpr int JW = D / 32;                              // column blocks
-  static_assert(D <= 128, "a strip and its result must fit one wavefront's registers");
+  static_assert(D <= 128 || sizeof(T) == 2, "a strip and its result must fit one wavefront's registers");
   constexpr int NSLAB = CH / S4_NCS;                      // slabs per source
   constexpr int SV = D * 2 * S4_NCS;                      // 16-byte vectors per slab
   constexpr int SU = (SV + S4_THREADS - 1) / S4_THREADS;  // per thread
@@ -845,11 +849,7 @@ int64_t wgrad_rows_per_slot(int64_t n, int slots) {
 
 template <typename T, bool TRANSB, int NA>
 static void launch_rows(const RowsGemm &g, dim3 grid, hipStream_t st) {
-  switch (g.d) {
-    case 64: k_gemm_rows<T, 64, TRANSB, NA><<<grid, RG_THREADS, 0, st>>>(g); break;
-    case 128: k_gemm_rows<T, 128, TRANSB, NA><<<grid, RG_THREADS, 0, st>>>(g); break;
-    default: k_gemm_rows<T, 256, TRANSB, NA><<<grid, RG_THREADS, 0, st>>>(g); break;
-  }
+  k_gemm_rows<T, 256, TRANSB, NA><<<grid, RG_THREADS, 0, st>>>(g);
 }
 
 // resident workgroups that fit on one CU (registers and LDS), from the runtime
@@ -907,15 +907,16 @@ static void launch_sum4(const RowsGemm &g, hipStream_t st) {
 gt_status launch_rows_gemm(gt_dtype dt, RowsGemm g, int nout, bool transb, hipStream_t st) {
   if (g.n == 0) return GT_OK;
   g.nout = nout;
-  if (transb && g.d <= 128) {   // the input gradient: four sources
-    // (at d = 256 the column-tiled kernel below measured faster: the slab
-    // kernel must split a strip over two wavefronts there)
+  if (transb && !(dt == GT_F32 && g.d == 256)) {   // the input gradient: four sources
+    // (fp32 at d = 256: a strip and its result do not fit the registers
+    // together; that case takes the column-tiled kernel below)
     if (dt == GT_F32) {
       if (g.d == 64) launch_sum4<float, 64>(g, st);
       else launch_sum4<float, 128>(g, st);
     } else {
       if (g.d == 64) launch_sum4<bf16_t, 64>(g, st);
-      else launch_sum4<bf16_t, 128>(g, st);
+      else if (g.d == 128) launch_sum4<bf16_t, 128>(g, st);
+      else launch_sum4<bf16_t, 256>(g, st);
     }
     GT_CHECK_LAUNCH();
     return GT_OK;
@@ -932,14 +933,10 @@ gt_status launch_rows_gemm(gt_dtype dt, RowsGemm g, int nout, bool transb, hipSt
     GT_CHECK_LAUNCH();
     return GT_OK;
   }
+  // fp32 at d = 256: the column-tiled kernel
   const dim3 grid((unsigned)cdiv(g.n, RG_ROWS));
-  if (dt == GT_F32) {
-    if (transb) launch_rows<float, true, 4>(g, grid, st);
-    else launch_rows<float, false, 1>(g, grid, st);
-  } else {
-    if (transb) launch_rows<bf16_t, true, 4>(g, grid, st);
-    else launch_rows<bf16_t, false, 1>(g, grid, st);
-  }
+  if (transb) launch_rows<float, true, 4>(g, grid, st);
+  else launch_rows<float, false, 1>(g, grid, st);
   GT_CHECK_LAUNCH();
   return GT_OK;
 }
