@@ -19,11 +19,10 @@
 // C[m][n] with n = l % 32 and m = 8 (v / 4) + 4 (l / 32) + v % 4.
 //
 // LDS tiles are rows of 16-byte chunks with an XOR swizzle on the chunk
-// index (no padding), chosen so that the operand reads (8 rows, one chunk
-// each) and the transposing writes of the staging code spread over the
-// banks.
+// index, chosen so that the operand reads (8 rows, one chunk each) and the
+// transposing writes of the staging code spread over the banks; the slab
+// tiles of the input gradient, whose rows are short, are padded instead.
 #include <algorithm>
-#include <type_traits>
 
 #include "device.hpp"
 #include "host.hpp"

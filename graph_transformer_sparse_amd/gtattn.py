@@ -180,9 +180,18 @@ class Graph:
 
 def gt_graph_prepare(indptr: torch.Tensor, indices: torch.Tensor, n_cols: int,
                      t_small: int | None = None, t_mid: int | None = None,
-                     chunk: int | None = None) -> Graph:
-    """Prepare a device CSR (int32 indptr/indices) for attention."""
+                     chunk: int | None = None, validate: bool | None = None) -> Graph:
+    """Prepare a device CSR (int32 indptr/indices) for attention.  With
+    validate (default: the environment variable GT_DEBUG=1) the CSR content
+    is checked on the GPU first (gt_csr_validate) and a malformed graph
+    raises instead of giving undefined results."""
     L = lib()
+    if validate is None:
+        validate = os.environ.get("GT_DEBUG", "0") == "1"
+    if validate:
+        code = gt_csr_validate(indptr, indices, n_cols)
+        if code != 0:
+            raise GTError(8, "gt_graph_prepare", f"malformed CSR (gt_csr_validate code {code})")
     d_small, d_mid, d_chunk = gt_default_thresholds()
     t_small = d_small if t_small is None else t_small
     t_mid = d_mid if t_mid is None else t_mid
