@@ -851,27 +851,42 @@ static void launch_rows(const RowsGemm &g, dim3 grid, hipStream_t st) {
   k_gemm_rows<T, 256, TRANSB, NA><<<grid, RG_THREADS, 0, st>>>(g);
 }
 
-// resident workgroups that fit on one CU (registers and LDS), from the runtime
+// Workgroups of a kernel that fit on one CU (registers and LDS), and the
+// CU count of the current device, from the runtime; each is queried once
+// per process (function-local statics initialise thread-safely).
+template <typename K>
+static int blocks_per_cu(K kernel, int threads) {
+  int nb = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, kernel, threads, 0) != hipSuccess || nb < 1)
+    nb = 1;
+  return nb;
+}
+
+static int device_cus() {
+  static const int cus = [] {
+    int dev = 0, n = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n < 1)
+      n = 256;
+    return n;
+  }();
+  return cus;
+}
+
 template <typename T, int D, bool RESID, int NZ>
 static int resident_per_cu() {
-  static int per_cu = 0;
-  if (per_cu == 0) {
-    int nb = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, k_rows_resident<T, D, RESID, NZ>,
-                                                     RR_THREADS, 0) != hipSuccess || nb < 1)
-      nb = 1;
-    per_cu = nb;
-  }
+  static const int per_cu = blocks_per_cu(k_rows_resident<T, D, RESID, NZ>, RR_THREADS);
   return per_cu;
 }
 
 template <typename T, int D, bool RESID, int NZ>
 static void launch_resident_k(const RowsGemm &g, hipStream_t st) {
-  // workgroups per (XCD, output split): fill the CUs of the XCD (32 each),
-  // but no more than the strips need
+  // workgroups per (XCD, output split): fill the CUs of the XCD (eight
+  // XCDs), but no more than the strips need
   const int nsplit = NZ == 1 ? g.nout : 1;
   const int64_t strips = cdiv(g.n, 32);
-  int64_t groups = std::max<int64_t>(1, (int64_t)resident_per_cu<T, D, RESID, NZ>() * 32 / nsplit);
+  const int64_t cus_per_xcd = std::max(1, device_cus() / 8);
+  int64_t groups = std::max<int64_t>(1, (int64_t)resident_per_cu<T, D, RESID, NZ>() * cus_per_xcd / nsplit);
   groups = std::max<int64_t>(1, std::min<int64_t>(groups, cdiv(strips, 8 * RR_WAVES)));
   const dim3 grid((unsigned)(8 * groups * nsplit));
   k_rows_resident<T, D, RESID, NZ><<<grid, RR_THREADS, 0, st>>>(g, (int)groups);
@@ -890,16 +905,9 @@ static void launch_resident(const RowsGemm &g, hipStream_t st) {
 // transb = false: one source (NA = 1); transb = true: four (NA = 4)
 template <typename T, int D>
 static void launch_sum4(const RowsGemm &g, hipStream_t st) {
-  static int per_cu = 0;
-  if (per_cu == 0) {
-    int nb = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, k_rows_sum4<T, D>, S4_THREADS, 0) !=
-            hipSuccess || nb < 1)
-      nb = 1;
-    per_cu = nb;
-  }
+  static const int per_cu = blocks_per_cu(k_rows_sum4<T, D>, S4_THREADS);
   const int64_t nblk = cdiv(g.n, S4_ROWS);
-  const int64_t grid = std::min<int64_t>(nblk, (int64_t)per_cu * 256);
+  const int64_t grid = std::min<int64_t>(nblk, (int64_t)per_cu * device_cus());
   k_rows_sum4<T, D><<<dim3((unsigned)grid), S4_THREADS, 0, st>>>(g);
 }
 
