@@ -256,10 +256,19 @@ __device__ inline int32_t row_of_edge(const int32_t *indptr, int64_t n_rows, int
   return (int32_t)lo;
 }
 
-__global__ void k_source_rows(const int32_t *indptr, int64_t n_rows, const int32_t *perm,
-                              int64_t nnz, int32_t *indices_t) {
+// The row of every CSR edge, in edge order: the threads of a wavefront
+// search for consecutive edges, so their binary searches walk nearly the
+// same path through indptr (shared, cached loads).
+__global__ void k_edge_rows(const int32_t *indptr, int64_t n_rows, int64_t nnz, int32_t *row_of) {
+  const int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (e < nnz) row_of[e] = row_of_edge(indptr, n_rows, (int32_t)e);
+}
+
+// indices_t[t] = the row of edge perm[t]
+__global__ void k_source_rows(const int32_t *row_of, const int32_t *perm, int64_t nnz,
+                              int32_t *indices_t) {
   const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (t < nnz) indices_t[t] = row_of_edge(indptr, n_rows, perm[t]);
+  if (t < nnz) indices_t[t] = row_of[perm[t]];
 }
 
 // ---------------------------------------------------------------------------
@@ -272,17 +281,25 @@ struct Misc {  // device counters in the meta buffer
   uint32_t csr_flags, csr_first;
 };
 
-// Maximum degree and tier counts: each wavefront reduces its lanes with
-// shuffles, then one lane per wavefront updates the counters.
-__global__ __launch_bounds__(256) void k_degree_stats(const int32_t *ptr, int64_t n,
-                                                      int32_t t_small, int32_t t_mid, Misc *m) {
-  const int64_t s = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+// Maximum degree and tier counts: each thread walks segments grid-strided,
+// wavefronts reduce with shuffles, workgroups through LDS, and one thread
+// per workgroup updates the counters (few enough workgroups that the
+// atomics on the four counters do not queue up).
+constexpr int DS_THREADS = 256, DS_MAX_BLOCKS = 1024;
+
+__global__ __launch_bounds__(DS_THREADS) void k_degree_stats(const int32_t *ptr, int64_t n,
+                                                             int32_t t_small, int32_t t_mid,
+                                                             Misc *m) {
+  __shared__ uint32_t red[DS_THREADS / WAVE][4];
   uint32_t d = 0, big = 0, mid = 0, small = 0;
-  if (s < n) {
-    d = (uint32_t)(ptr[s + 1] - ptr[s]);
-    big = (int32_t)d > t_mid;
-    mid = !big && (int32_t)d > t_small;
-    small = !big && !mid;
+  for (int64_t s = (int64_t)blockIdx.x * DS_THREADS + threadIdx.x; s < n;
+       s += (int64_t)gridDim.x * DS_THREADS) {
+    const int32_t dd = ptr[s + 1] - ptr[s];
+    d = max(d, (uint32_t)dd);
+    const bool b = dd > t_mid, md = !b && dd > t_small;
+    big += b;
+    mid += md;
+    small += !b && !md;
   }
 #pragma unroll
   for (int o = WAVE / 2; o > 0; o >>= 1) {
@@ -291,7 +308,21 @@ __global__ __launch_bounds__(256) void k_degree_stats(const int32_t *ptr, int64_
     mid += __shfl_xor((int)mid, o);
     small += __shfl_xor((int)small, o);
   }
+  const int w = threadIdx.x / WAVE;
   if ((threadIdx.x & (WAVE - 1)) == 0) {
+    red[w][0] = d;
+    red[w][1] = big;
+    red[w][2] = mid;
+    red[w][3] = small;
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    for (int k = 1; k < DS_THREADS / WAVE; ++k) {
+      d = max(d, red[k][0]);
+      big += red[k][1];
+      mid += red[k][2];
+      small += red[k][3];
+    }
     atomicMax(&m->max_degree, d);
     if (big) atomicAdd(&m->n_big, big);
     if (mid) atomicAdd(&m->n_mid, mid);
@@ -347,7 +378,8 @@ static gt_status build_schedule(const int32_t *ptr, int64_t n, int32_t t_small, 
   GT_HIP(hipMemsetAsync(misc_d, 0, sizeof(Misc), s));
   const int TB = 256;
   if (n > 0) {
-    k_degree_stats<<<dim3((unsigned)cdiv(n, TB)), dim3(TB), 0, s>>>(ptr, n, t_small, t_mid, misc_d);
+    const int64_t nblk = std::min<int64_t>(cdiv(n, DS_THREADS), DS_MAX_BLOCKS);
+    k_degree_stats<<<dim3((unsigned)nblk), dim3(DS_THREADS), 0, s>>>(ptr, n, t_small, t_mid, misc_d);
     GT_CHECK_LAUNCH();
   }
   Misc m;
@@ -485,7 +517,12 @@ extern "C" gt_status gt_graph_prepare(const int32_t *indptr, const int32_t *indi
   GT_CHECK_LAUNCH();
   if (nnz > 0) {
     GT_HIP(hipMemcpyAsync(g.perm, vs, sizeof(int32_t) * (size_t)nnz, hipMemcpyDeviceToDevice, s));
-    k_source_rows<<<dim3((unsigned)cdiv(nnz, TB)), dim3(TB), 0, s>>>(indptr, n_rows, g.perm, nnz,
+    // the sort buffers are free again (stream order): rows of the edges in
+    // edge order into one of them, then gathered through perm
+    int32_t *row_of = (int32_t *)(vs == b.vA ? b.vB : b.vA);
+    k_edge_rows<<<dim3((unsigned)cdiv(nnz, TB)), dim3(TB), 0, s>>>(indptr, n_rows, nnz, row_of);
+    GT_CHECK_LAUNCH();
+    k_source_rows<<<dim3((unsigned)cdiv(nnz, TB)), dim3(TB), 0, s>>>(row_of, g.perm, nnz,
                                                                       g.indices_t);
     GT_CHECK_LAUNCH();
   }
