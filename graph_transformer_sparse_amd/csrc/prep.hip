@@ -142,19 +142,33 @@ __global__ __launch_bounds__(SORT_THREADS) void k_sort_hist(const uint32_t *keys
 
 // Scatter a tile to its sorted positions.  offs = exclusive scan of hist
 // (digit-major), so offs[d * nblk + b] is where the digit-d items of tile b
-// start.  Inside a tile, items keep their order: rounds go in order, and
-// within a round an item's rank among equal digits counts the earlier waves
-// and the lower lanes of its own wave (found by matching the 8 digit bits
-// with ballots).  vin == nullptr means value = item index.
+// start.  The tile is first sorted by digit in LDS: an item's place is the
+// start of its digit in the tile plus its rank among equal digits, which
+// keeps the items' order (rounds go in order, and within a round the rank
+// counts the earlier waves and the lower lanes of its own wave, found by
+// matching the 8 digit bits with ballots).  Then consecutive threads copy
+// consecutive LDS slots out, so each digit's run leaves as contiguous
+// stores.  vin == nullptr means value = item index.
 __global__ __launch_bounds__(SORT_THREADS) void k_sort_scatter(
     const uint32_t *kin, const uint32_t *vin, uint32_t *kout, uint32_t *vout, int64_t n,
     int shift, const uint32_t *offs, int64_t nblk) {
-  __shared__ uint32_t run[RADIX];
+  __shared__ uint32_t sk[SORT_TILE], sv[SORT_TILE];
+  __shared__ uint32_t tstart[RADIX], run[RADIX], gstart[RADIX];
   __shared__ uint32_t wc[SORT_THREADS / WAVE][RADIX];
   const int t = threadIdx.x, wv = t / WAVE;
-  run[t] = offs[(int64_t)t * nblk + blockIdx.x];
-  const uint64_t lt = (1ull << (t & (WAVE - 1))) - 1ull;
   const int64_t base = (int64_t)blockIdx.x * SORT_TILE;
+  const int64_t tile_n = std::min<int64_t>(SORT_TILE, n - base);
+  // this tile's count of digit t, from consecutive entries of the
+  // digit-major offsets (the last entry ends at n)
+  const int64_t o = (int64_t)t * nblk + blockIdx.x;
+  const uint32_t g0 = offs[o];
+  const uint32_t g1 = (o + 1 < RADIX * nblk) ? offs[o + 1] : (uint32_t)n;
+  uint32_t total;
+  const uint32_t ts = block_excl_scan(g1 - g0, &total);
+  tstart[t] = ts;
+  run[t] = ts;
+  gstart[t] = g0;
+  const uint64_t lt = (1ull << (t & (WAVE - 1))) - 1ull;
   for (int r = 0; r < SORT_ROUNDS; ++r) {
 #pragma unroll
     for (int w = 0; w < SORT_THREADS / WAVE; ++w) wc[w][t] = 0;
@@ -176,14 +190,22 @@ __global__ __launch_bounds__(SORT_THREADS) void k_sort_scatter(
     if (valid) {
       uint32_t pos = run[d] + (uint32_t)rank;
       for (int w = 0; w < wv; ++w) pos += wc[w][d];
-      kout[pos] = key;
-      vout[pos] = vin ? vin[i] : (uint32_t)i;
+      sk[pos] = key;
+      sv[pos] = vin ? vin[i] : (uint32_t)i;
     }
     __syncthreads();
     uint32_t add = 0;
 #pragma unroll
     for (int w = 0; w < SORT_THREADS / WAVE; ++w) add += wc[w][t];
     run[t] += add;
+  }
+  __syncthreads();
+  for (int j = t; j < tile_n; j += SORT_THREADS) {
+    const uint32_t key = sk[j];
+    const uint32_t d = (key >> shift) & (RADIX - 1);
+    const uint32_t pos = gstart[d] + ((uint32_t)j - tstart[d]);
+    kout[pos] = key;
+    vout[pos] = sv[j];
   }
 }
 
