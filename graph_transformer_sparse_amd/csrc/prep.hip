@@ -278,12 +278,40 @@ __device__ inline int32_t row_of_edge(const int32_t *indptr, int64_t n_rows, int
   return (int32_t)lo;
 }
 
-// The row of every CSR edge, in edge order: the threads of a wavefront
-// search for consecutive edges, so their binary searches walk nearly the
-// same path through indptr (shared, cached loads).
-__global__ void k_edge_rows(const int32_t *indptr, int64_t n_rows, int64_t nnz, int32_t *row_of) {
-  const int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (e < nnz) row_of[e] = row_of_edge(indptr, n_rows, (int32_t)e);
+// The row of every CSR edge, in edge order.  A workgroup takes ER_TILE
+// consecutive edges: two searches give the rows of its first and last edge,
+// the indptr entries between them go to LDS, and each edge then searches
+// only those (the global search per edge stays as the fallback for a tile
+// that spans more rows than fit, which takes many empty rows).
+constexpr int ER_THREADS = 256, ER_TILE = 4096, ER_ROWS = 4096;
+
+__global__ __launch_bounds__(ER_THREADS) void k_edge_rows(const int32_t *indptr, int64_t n_rows,
+                                                          int64_t nnz, int32_t *row_of) {
+  __shared__ int32_t ip[ER_ROWS + 1];
+  __shared__ int32_t r01[2];
+  const int64_t e0 = (int64_t)blockIdx.x * ER_TILE;
+  const int64_t e1 = std::min<int64_t>(e0 + ER_TILE, nnz);   // exclusive
+  if (threadIdx.x < 2)
+    r01[threadIdx.x] = row_of_edge(indptr, n_rows, (int32_t)(threadIdx.x == 0 ? e0 : e1 - 1));
+  __syncthreads();
+  const int32_t r0 = r01[0], r1 = r01[1];
+  const int64_t nr = (int64_t)r1 - r0 + 1;                   // rows r0 .. r1
+  if (nr <= ER_ROWS) {
+    for (int64_t k = threadIdx.x; k <= nr; k += ER_THREADS) ip[k] = indptr[r0 + k];
+    __syncthreads();
+    for (int64_t e = e0 + threadIdx.x; e < e1; e += ER_THREADS) {
+      int lo = 0, hi = (int)nr;            // last k with ip[k] <= e, in [lo, hi)
+      while (hi - lo > 1) {
+        const int mid = (lo + hi) >> 1;
+        if (ip[mid] <= e) lo = mid;
+        else hi = mid;
+      }
+      row_of[e] = r0 + lo;
+    }
+  } else {
+    for (int64_t e = e0 + threadIdx.x; e < e1; e += ER_THREADS)
+      row_of[e] = row_of_edge(indptr, n_rows, (int32_t)e);
+  }
 }
 
 // indices_t[t] = the row of edge perm[t]
@@ -368,25 +396,27 @@ __global__ void k_piece_counts(const int32_t *ptr, const int32_t *order, int64_t
   split[k] = c > 1 ? 1u : 0u;
 }
 
-__global__ void k_write_items(const int32_t *ptr, const int32_t *order, int64_t nb,
-                              const uint32_t *nch_in, const uint32_t *item_off,
-                              const uint32_t *merge_off, int32_t chunk, int32_t *items,
-                              int32_t *merges) {
-  const int64_t k = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+// One wavefront per big segment; its lanes write the segment's pieces.
+constexpr int WI_THREADS = 256;
+
+__global__ __launch_bounds__(WI_THREADS) void k_write_items(
+    const int32_t *ptr, const int32_t *order, int64_t nb, const uint32_t *item_off,
+    const uint32_t *merge_off, int32_t chunk, int32_t *items, int32_t *merges) {
+  const int64_t k = (int64_t)blockIdx.x * (WI_THREADS / WAVE) + threadIdx.x / WAVE;
+  const int lane = threadIdx.x & (WAVE - 1);
   if (k >= nb) return;
   const int32_t sg = order[k];
   const int64_t p0 = ptr[sg], d = ptr[sg + 1] - p0;
   const int64_t nch = (d + chunk - 1) / chunk;
   const int64_t off = item_off[k];
-  (void)nch_in;
-  for (int64_t c = 0; c < nch; ++c) {
+  for (int64_t c = lane; c < nch; c += WAVE) {
     int32_t *it = items + 4 * (off + c);
     it[0] = sg;
     it[1] = (int32_t)(p0 + (c * d) / nch);
     it[2] = (int32_t)(p0 + ((c + 1) * d) / nch);
     it[3] = nch > 1 ? (int32_t)(off + c) : -1;
   }
-  if (nch > 1) {
+  if (nch > 1 && lane == 0) {
     int32_t *mg = merges + 3 * (int64_t)merge_off[k];
     mg[0] = sg;
     mg[1] = (int32_t)off;
@@ -428,8 +458,8 @@ static gt_status build_schedule(const int32_t *ptr, int64_t n, int32_t t_small, 
     if (st != GT_OK) return st;
     st = excl_scan(split, moff, nb, b.bsum, &misc_d->n_merges, s);
     if (st != GT_OK) return st;
-    k_write_items<<<dim3((unsigned)cdiv(nb, TB)), dim3(TB), 0, s>>>(
-        ptr, out->order, nb, nch, ioff, moff, chunk, out->items, out->merges);
+    k_write_items<<<dim3((unsigned)cdiv(nb, WI_THREADS / WAVE)), dim3(WI_THREADS), 0, s>>>(
+        ptr, out->order, nb, ioff, moff, chunk, out->items, out->merges);
     GT_CHECK_LAUNCH();
     GT_HIP(hipMemcpyAsync(&m, misc_d, sizeof(Misc), hipMemcpyDeviceToHost, s));
     GT_HIP(hipStreamSynchronize(s));
@@ -542,7 +572,8 @@ extern "C" gt_status gt_graph_prepare(const int32_t *indptr, const int32_t *indi
     // the sort buffers are free again (stream order): rows of the edges in
     // edge order into one of them, then gathered through perm
     int32_t *row_of = (int32_t *)(vs == b.vA ? b.vB : b.vA);
-    k_edge_rows<<<dim3((unsigned)cdiv(nnz, TB)), dim3(TB), 0, s>>>(indptr, n_rows, nnz, row_of);
+    k_edge_rows<<<dim3((unsigned)cdiv(nnz, ER_TILE)), dim3(ER_THREADS), 0, s>>>(indptr, n_rows,
+                                                                               nnz, row_of);
     GT_CHECK_LAUNCH();
     k_source_rows<<<dim3((unsigned)cdiv(nnz, TB)), dim3(TB), 0, s>>>(row_of, g.perm, nnz,
                                                                       g.indices_t);
