@@ -31,6 +31,14 @@ def _graphs():
     out.append(("hubs", ip, ix, 3000))
     ip, ix = I.graph_for(I.CONFIGS["tiny"])
     out.append(("tiny", ip, ix, 2000))
+    # edges only every 7000th row (thousands of empty rows between), one row
+    # long enough to fill several 4096-edge tiles of the row-of-edge pass
+    rows = [[] for _ in range(60000)]
+    for r in range(0, 60000, 7000):
+        rows[r] = [r % 900, 1000 + r % 7]
+    rows[14000] = list(range(0, 9000))
+    ip, ix = I.csr_from_rows(rows, 9000)
+    out.append(("sparse_rows", ip, ix, 9000))
     return out
 
 
