@@ -247,6 +247,7 @@ def main():
     ach = kern[dominant]["GBps"]
     traffic = traffic_record(dominant, cfg.name)
     total_model = sum(model.values())
+    graph_ms = graph_replay_ms(step, args.steps)
 
     line = {
         "metric": "GEdges/s fused sparse-attn fwd+bwd, 1 MI355X; achieved HBM GB/s vs peak",
@@ -272,11 +273,39 @@ def main():
                    "step_GBps": total_model / (ms_step * 1e-3) / 1e9,
                    "step_frac": total_model / (ms_step * 1e-3) / 1e9 / HBM_PEAK_GBS,
                    "kernels": kern, "prep_ms": prep_ms, "input_gen_s": gen_s,
-                   "kernel_source_hash": kernel_source_hash()},
+                   "kernel_source_hash": kernel_source_hash(),
+                   "graph_replay_ms_per_step": graph_ms},
     }
     if args.cpu_budget > 0:
         line["cpu_baseline"] = cpu_baseline(P, args.cpu_budget)
     print(json.dumps(line), flush=True)
+
+
+def graph_replay_ms(step, reps):
+    """The same step captured once into a HIP graph and replayed `reps`
+    times (after the timed region; it does not change `value`): what a
+    caller that captures the step saves in launch overhead.  None if the
+    capture fails."""
+    import torch
+    try:
+        s = torch.cuda.Stream()
+        s.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(s):
+            step()
+        torch.cuda.current_stream().wait_stream(s)
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            step()
+        graph.replay()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(reps):
+            graph.replay()
+        torch.cuda.synchronize()
+        return (time.perf_counter() - t0) * 1e3 / reps
+    except Exception as e:      # report, never fail the benchmark for it
+        print(f"graph replay skipped: {e}", file=sys.stderr)
+        return None
 
 
 def T_np(t):
