@@ -37,7 +37,9 @@
  *   - `stream` is a hipStream_t (NULL = the default stream).  Calls enqueue
  *     work on it and return, except gt_graph_prepare and gt_csr_validate,
  *     which synchronise that stream before returning (both run once per
- *     graph).
+ *     graph).  gt_attn_fwd and gt_attn_bwd enqueue kernels only (no
+ *     memsets, copies or host synchronisation), so a caller may capture
+ *     them into a HIP graph and replay it.
  *   - Dense features are row-major [n, heads, head_dim] (node-major, heads
  *     contiguous), in the dtype `dt`; rows start 16-byte aligned.
  *     Supported: head_dim in {16, 32, 64}, heads in {1, 2, 4, 8}, and
