@@ -280,15 +280,17 @@ __global__ __launch_bounds__(RG_THREADS) void k_gemm_rows(RowsGemm g) {
 // one-source row GEMM with the weight resident in LDS: C_z = A W_z (+ R).
 //
 // Used where W fits in LDS (D * D elements of at most 128 KB: bf16 up to
-// D = 256, fp32 up to D = 128).  A workgroup of 8 wavefronts stages one W_z
-// once, as [n][k] with the chunk swizzle, and its wavefronts then run
-// without barriers: each takes 32-row strips of A in turn and holds the
+// D = 256, fp32 up to D = 128).  A workgroup of 8 wavefronts stages its
+// weights once, as [n][k] with the chunk swizzle: all NZ = 3 of Q/K/V where
+// they fit together, else the one W_z of its output.  Its wavefronts then
+// run without barriers: each takes 32-row strips of A in turn and holds the
 // strip in registers (operand layout as above) while the next strip's loads
 // are in flight; for each 32-column block it runs CH MFMAs with the strip as
 // the B operand and the weight rows as A, so that lane l ends up with row
 // l % 32 and columns 8 g + 4 (l / 32) + i of the block (g, i < 4): four
-// contiguous values, written as one 8- (bf16) or 16-byte (fp32) store.  The
-// residual of a block is fetched one or two blocks ahead.  Every global
+// contiguous values.  fp32 writes them as one 16-byte store; bf16 trades a
+// group between lane halves to write 16 bytes too, a pair of blocks at a
+// time.  The residual of a block is fetched one or two blocks ahead.  Every global
 // access goes through a buffer resource bounded to the strip, so rows past
 // n read as zero and their stores are dropped without a branch (which also
 // keeps the memory counters exact).  Workgroups that share strips for
@@ -337,12 +339,6 @@ template <> struct OutVec<bf16_t> {
   __device__ static inline void add(float (&x)[4], const type &v) {
     x[0] += __uint_as_float(v.x << 16); x[1] += __uint_as_float(v.x & 0xffff0000u);
     x[2] += __uint_as_float(v.y << 16); x[3] += __uint_as_float(v.y & 0xffff0000u);
-  }
-  __device__ static inline void store(__amdgpu_buffer_rsrc_t r, int o, const float (&x)[4]) {
-    const uint2 v = make_uint2(bf16_rne(x[0]) | (bf16_rne(x[1]) << 16),
-                               bf16_rne(x[2]) | (bf16_rne(x[3]) << 16));
-    __builtin_amdgcn_raw_buffer_store_b64(
-        __builtin_bit_cast(decltype(__builtin_amdgcn_raw_buffer_load_b64(r, 0, 0, 0)), v), r, o, 0, 0);
   }
 };
 
