@@ -338,22 +338,33 @@ def _cache_dir():
     return d if d else None
 
 
+_GRAPHS = {}   # the named graphs generated in this process
+
+
+def named_graph(cfg: Config):
+    """graph_for(cfg), generated once per process (and read from / written
+    to the directory GT_INPUT_CACHE names, if set)."""
+    if cfg.name in _GRAPHS:
+        return _GRAPHS[cfg.name]
+    cache = _cache_dir()
+    path = os.path.join(cache, f"graph_{cfg.name}.npz") if cache else None
+    if path and os.path.exists(path):
+        with np.load(path) as z:
+            graph = (z["indptr"], z["indices"])
+    else:
+        graph = graph_for(cfg)
+        if path:
+            os.makedirs(cache, exist_ok=True)
+            tmp = path + ".tmp.npz"
+            np.savez(tmp, indptr=graph[0], indices=graph[1])
+            os.replace(tmp, path)
+    _GRAPHS[cfg.name] = graph
+    return graph
+
+
 def make_problem(cfg: Config, graph=None) -> Problem:
     """All inputs of one configuration.  ``graph`` overrides the graph."""
-    if graph is None:
-        cache = _cache_dir()
-        path = os.path.join(cache, f"graph_{cfg.name}.npz") if cache else None
-        if path and os.path.exists(path):
-            with np.load(path) as z:
-                graph = (z["indptr"], z["indices"])
-        else:
-            graph = graph_for(cfg)
-            if path:
-                os.makedirs(cache, exist_ok=True)
-                tmp = path + ".tmp.npz"
-                np.savez(tmp, indptr=graph[0], indices=graph[1])
-                os.replace(tmp, path)
-    indptr, indices = graph
+    indptr, indices = named_graph(cfg) if graph is None else graph
     H, dh = cfg.heads, cfg.head_dim
     Q = features(cfg.idx, S_Q, cfg.n_rows, H, dh, cfg.dtype)
     K = features(cfg.idx, S_K, cfg.n_cols, H, dh, cfg.dtype)

@@ -132,3 +132,28 @@ def test_big_config_sampled(name):
         assert_close(o["dB"][eb], rB, rt, "dbias", head_axis=1)
     print(f"{name}: invariants", flush=True)
     _invariants(P, o, rt)
+
+
+@pytest.mark.parametrize("name", ["mid", "large", "hub", "shard"])
+def test_prep_full_configs(name):
+    """Graph preparation at the full workload sizes, default thresholds:
+    the CSR transpose and both degree-ordered schedules bit-exact with the
+    oracle."""
+    cfg = I.CONFIGS[name]
+    ip, ix = I.named_graph(cfg)
+    print(f"prep {name}: gpu", flush=True)
+    g = T.gt_graph_prepare(torch.from_numpy(ip).cuda(), torch.from_numpy(ix).cuda(), cfg.n_cols)
+    torch.cuda.synchronize()
+    print(f"prep {name}: oracle transpose", flush=True)
+    pt, it, pm = O.transpose(ip, ix, cfg.n_cols)
+    assert np.array_equal(g.indptr_t.cpu().numpy(), pt)
+    assert np.array_equal(g.indices_t.cpu().numpy(), it)
+    assert np.array_equal(g.perm.cpu().numpy(), pm)
+    ts, tm, ch = T.gt_default_thresholds()
+    print(f"prep {name}: oracle schedules", flush=True)
+    for which, ptr in (("rows", ip), ("cols", pt)):
+        got, want = g.schedule(which), O.schedule(ptr, ts, tm, ch)
+        assert np.array_equal(got["order"].cpu().numpy(), want["order"]), which
+        assert tuple(got["counts"]) == tuple(int(c) for c in want["counts"]), which
+        assert np.array_equal(got["items"].cpu().numpy(), want["items"]), which
+        assert np.array_equal(got["merges"].cpu().numpy(), want["merges"]), which

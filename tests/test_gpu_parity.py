@@ -101,12 +101,18 @@ def test_scale_other_than_default():
 
 
 def test_bitwise_determinism():
+    """Two runs, and a run on another stream, give bitwise-equal outputs."""
     P = I.make_problem(I.CONFIGS["tiny"])
     a = run_gpu(P, (2, 6, 4))
     b = run_gpu(P, (2, 6, 4))
-    for x, y in zip(a, b):
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        c = run_gpu(P, (2, 6, 4))
+    torch.cuda.synchronize()
+    for x, y, z in zip(a, b, c):
         if x is not None:
-            assert torch.equal(x, y)
+            assert torch.equal(x, y) and torch.equal(x, z)
 
 
 def test_autograd_function_matches_abi():
