@@ -188,6 +188,12 @@ def gt_graph_prepare(indptr: torch.Tensor, indices: torch.Tensor, n_cols: int,
     L = lib()
     if validate is None:
         validate = os.environ.get("GT_DEBUG", "0") == "1"
+    # tuning overrides of the schedule's defaults (GT_TIER_SMALL, GT_TIER_MID,
+    # GT_TIER_CHUNK); explicit arguments win
+    env = lambda k: int(os.environ[k]) if os.environ.get(k) else None
+    t_small = env("GT_TIER_SMALL") if t_small is None else t_small
+    t_mid = env("GT_TIER_MID") if t_mid is None else t_mid
+    chunk = env("GT_TIER_CHUNK") if chunk is None else chunk
     if validate:
         code = gt_csr_validate(indptr, indices, n_cols)
         if code != 0:

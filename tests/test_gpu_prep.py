@@ -123,3 +123,17 @@ def test_prepare_validates_on_request():
         T.gt_graph_prepare(dev(ip), dev(bad), 4, validate=True)
     g = T.gt_graph_prepare(dev(ip), dev(ix), 4, validate=True)
     assert g.nnz == ix.size
+
+
+def test_tier_env_overrides(monkeypatch):
+    """GT_TIER_SMALL / GT_TIER_MID / GT_TIER_CHUNK replace the schedule's
+    defaults; explicit arguments still win."""
+    ip, ix = I.csr_from_rows([[0, 2], [1], [], [0, 1, 3]], 4)
+    monkeypatch.setenv("GT_TIER_SMALL", "1")
+    monkeypatch.setenv("GT_TIER_MID", "2")
+    monkeypatch.setenv("GT_TIER_CHUNK", "2")
+    g = T.gt_graph_prepare(dev(ip), dev(ix), 4)
+    assert (g.st.t_small, g.st.t_mid, g.st.chunk) == (1, 2, 2)
+    _check_sched(g.schedule("rows"), ip, 1, 2, 2)
+    g = T.gt_graph_prepare(dev(ip), dev(ix), 4, 0, 8, 8)
+    assert (g.st.t_small, g.st.t_mid, g.st.chunk) == (0, 8, 8)
