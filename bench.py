@@ -319,9 +319,10 @@ def proj_model(n, d, s):
     """Algorithmic bytes and flops of each projection kernel (every node
     array read or written once, weights once, the weight gradient's per-slot
     fp32 partials written and read once; the slot count is the library's:
-    a multiple of 8, at most 64 (d = 256) or 128, at most the 32-row steps)."""
+    a multiple of 8, at most 64 (d = 256 or float32) or 128, at most the
+    32-row steps)."""
     steps = -(-max(n, 1) // 32)
-    chunks = min(64 if d >= 256 else 128, -(-steps // 8) * 8)
+    chunks = min(64 if (d >= 256 or s == 4) else 128, -(-steps // 8) * 8)
     nd = n * d * s
     return {
         "proj_qkv": (4 * nd + 3 * d * d * s, 3 * 2 * n * d * d),

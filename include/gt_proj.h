@@ -22,7 +22,7 @@
  * The products run on the matrix cores with float32 accumulation; bf16
  * outputs are rounded to nearest even.  Results are bitwise deterministic:
  * the weight gradients sum per-slot partial products (slots of contiguous
- * node rows, a function of n and d only) in slot order.
+ * node rows, a function of n, d and dt only) in slot order.
  * Errors: GT_E_NULL, GT_E_ALIGN, GT_E_DTYPE, GT_E_SHAPE (d), GT_E_ARG (n),
  * GT_E_WORKSPACE, GT_E_HIP.
  */
@@ -51,7 +51,8 @@ gt_status gt_proj_bwd_data(int64_t n, int32_t d, gt_dtype dt, const void *dZ, co
                            const void *dK, const void *dV, const void *Wo, const void *Wq,
                            const void *Wk, const void *Wv, void *dX, void *stream);
 
-/* Bytes of `work` gt_proj_bwd_weight needs (per-slot partial products). */
+/* Bytes of `work` gt_proj_bwd_weight needs (per-slot partial products),
+ * enough for either dtype. */
 size_t gt_proj_work_bytes(int64_t n, int32_t d);
 
 /* dW_o = X^T dZ, dW_Q = X^T dQ, dW_K = X^T dK, dW_V = X^T dV (float32). */
