@@ -112,25 +112,51 @@ def cpu_baseline(P, budget_s: float):
         O.bwd(ip, ix, cfg.n_cols, q, K, V, dy, bias, P.scale)
         return time.perf_counter() - t, e
 
-    R = cfg.n_rows
-    k = min(R, 4096)
-    t, e = run(k)
-    while t < 0.5 and k < R:
-        k = min(R, k * 4)
+    def sized(budget):
+        R = cfg.n_rows
+        k = min(R, 4096)
         t, e = run(k)
-    if k < R and t < budget_s:
-        k = min(R, int(k * budget_s / max(t, 1e-3)))
-        t, e = run(k)
-    runs, total = 1, t
-    while total < budget_s:      # the whole workload is cheaper than the budget: repeat it
-        t, e = run(k)
-        runs += 1
-        total += t
-    return {"value": e * runs / total / 1e9, "unit": "GEdges/s", "cores": O.threads(),
-            "kind": "oracle",
-            "sample": (f"rows 0..{k - 1} of the {cfg.name} workload ({e} of {P.nnz} edges, "
-                       f"all {cfg.n_cols} key/value rows), fwd+bwd in float64, {runs} run(s) "
-                       f"in {total:.1f} s")}
+        while t < 0.5 * budget / 15 and k < R:
+            k = min(R, k * 4)
+            t, e = run(k)
+        if k < R and t < budget:
+            k = min(R, int(k * budget / max(t, 1e-3)))
+            t, e = run(k)
+        runs, total = 1, t
+        while total < budget:    # the whole workload is cheaper than the budget: repeat it
+            t, e = run(k)
+            runs += 1
+            total += t
+        return k, e, runs, total
+
+    k, e, runs, total = sized(budget_s)
+    cores = O.threads()
+    out = {"value": e * runs / total / 1e9, "unit": "GEdges/s", "cores": cores,
+           "kind": "oracle",
+           "sample": (f"rows 0..{k - 1} of the {cfg.name} workload ({e} of {P.nnz} edges, "
+                      f"all {cfg.n_cols} key/value rows), fwd+bwd in float64, {runs} run(s) "
+                      f"in {total:.1f} s"),
+           "cpu": cpu_model()}
+    # the same oracle on one thread, on a quarter of the budget
+    O.set_threads(1)
+    try:
+        k1, e1, runs1, total1 = sized(budget_s / 4)
+    finally:
+        O.set_threads(cores)
+    out["single_thread"] = {"value": e1 * runs1 / total1 / 1e9, "unit": "GEdges/s",
+                            "sample": f"rows 0..{k1 - 1}, {runs1} run(s) in {total1:.1f} s"}
+    return out
+
+
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for ln in f:
+                if ln.startswith("model name"):
+                    return ln.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
 
 
 def main():
@@ -231,14 +257,19 @@ def main():
     # timed region: only the dominant kernel carries events
     T.prof_reset()
     T.prof_enable([dominant])
+    cur = torch.cuda.current_stream()
+    marks = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for _ in range(args.steps):
+    marks[0].record(cur)
+    for i in range(args.steps):
         step()
+        marks[i + 1].record(cur)
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
     T.prof_enable(False)
     ms_step = elapsed * 1e3 / args.steps
+    per_step = sorted(marks[i].elapsed_time(marks[i + 1]) for i in range(args.steps))
     kern[dominant] = kernel_times()[dominant]
     for k in model:
         if k in kern:
@@ -272,6 +303,9 @@ def main():
         "detail": {"step_model_GB": total_model / 1e9,
                    "step_GBps": total_model / (ms_step * 1e-3) / 1e9,
                    "step_frac": total_model / (ms_step * 1e-3) / 1e9 / HBM_PEAK_GBS,
+                   "step_ms_events": {"mean": sum(per_step) / len(per_step),
+                                      "min": per_step[0],
+                                      "median": per_step[len(per_step) // 2]},
                    "kernels": kern, "prep_ms": prep_ms, "input_gen_s": gen_s,
                    "kernel_source_hash": kernel_source_hash(),
                    "graph_replay_ms_per_step": graph_ms},

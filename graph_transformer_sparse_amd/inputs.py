@@ -416,3 +416,58 @@ def layer_inputs(cfg_idx: int, n: int, d: int, dtype: str):
     W = {k: draw(s, (d, d), d ** -0.5) for k, s in (("q", S_WQ), ("k", S_WK), ("v", S_WV), ("o", S_WO))}
     dZ = draw(S_DZ, (n, d), 1.0)
     return X, W, dZ
+
+
+# ---------------------------------------------------------------------------
+# periodic circulant problems (tests at the maximum sizes)
+# ---------------------------------------------------------------------------
+def circulant_offsets(seed: int, n: int, period: int, degree: int) -> np.ndarray:
+    """Offsets o_0 = 0, o_1 .. o_{degree-1} of a circulant graph on n nodes
+    (row i links to (i + o_k) mod n; n a multiple of `period`, degree <=
+    period).  The residues o_k mod period are distinct (0, then degree - 1
+    drawn without replacement) and each gets a multiple of the period drawn
+    over [0, n), so a row's edges reach across the whole node range.  With
+    features periodic in the node index, every output of the graph is then
+    periodic too, and equals that of the `period`-node circulant graph with
+    offsets o_k mod period."""
+    assert n % period == 0 and 1 <= degree <= min(period, 255)
+    rng = rng_for(seed, S_GRAPH)
+    res = np.concatenate([[0], rng.choice(np.arange(1, period), degree - 1, replace=False)])
+    mult = np.concatenate([[0], rng.integers(0, n // period, degree - 1)])
+    return (res + period * mult).astype(np.int64)
+
+
+def circulant_csr(n: int, offsets, bias_table=None, device="cpu", row_block: int = 1 << 20):
+    """The circulant graph on n nodes as CSR torch tensors on `device`: row i
+    holds the columns (i + o_k) mod n in ascending order.  Returns (indptr
+    int32 [n+1], indices int32 [n*deg], slot uint8 [n*deg] = the offset index
+    k of each stored edge, bias float32 [n*deg, H] = bias_table[i mod P, k]
+    (P = bias_table.shape[0]) or None).  Built in blocks of rows."""
+    import torch
+    o = torch.as_tensor(np.asarray(offsets, np.int64), device=device)
+    deg = int(o.numel())
+    assert len(set(int(x) % n for x in np.asarray(offsets))) == deg, "offsets collide mod n"
+    indptr = torch.arange(0, n + 1, dtype=torch.int64, device=device).mul_(deg).to(torch.int32)
+    indices = torch.empty(n * deg, dtype=torch.int32, device=device)
+    slot = torch.empty(n * deg, dtype=torch.uint8, device=device)
+    bias = None
+    if bias_table is not None:
+        bt = torch.as_tensor(np.ascontiguousarray(bias_table, np.float32), device=device)
+        per, H = bt.shape[0], bt.shape[2]
+        bias = torch.empty((n * deg, H), dtype=torch.float32, device=device)
+    for r0 in range(0, n, row_block):
+        r1 = min(n, r0 + row_block)
+        rows = torch.arange(r0, r1, dtype=torch.int64, device=device)
+        cols, k = torch.sort((rows[:, None] + o[None, :]) % n, dim=1)
+        indices[r0 * deg:r1 * deg] = cols.reshape(-1).to(torch.int32)
+        slot[r0 * deg:r1 * deg] = k.reshape(-1).to(torch.uint8)
+        if bias is not None:
+            b = bt[rows % per]                                   # [rows, deg, H] by offset
+            bias[r0 * deg:r1 * deg] = torch.gather(b, 1, k[:, :, None].expand(-1, -1, H)).reshape(-1, H)
+    return indptr, indices, slot, bias
+
+
+def ternary(seed: int, stream: int, shape) -> np.ndarray:
+    """Values drawn uniformly from {-1, 0, 1} as float32 (exact in bf16):
+    products and sums of them stay integers, exact in float32 below 2^24."""
+    return rng_for(seed, stream).integers(-1, 2, shape).astype(np.float32)
