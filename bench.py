@@ -279,6 +279,7 @@ def main():
     traffic = traffic_record(dominant, cfg.name)
     total_model = sum(model.values())
     graph_ms = graph_replay_ms(step, args.steps)
+    copy_gbps = copy_rate_gbps()
 
     line = {
         "metric": "GEdges/s fused sparse-attn fwd+bwd, 1 MI355X; achieved HBM GB/s vs peak",
@@ -308,11 +309,32 @@ def main():
                                       "median": per_step[len(per_step) // 2]},
                    "kernels": kern, "prep_ms": prep_ms, "input_gen_s": gen_s,
                    "kernel_source_hash": kernel_source_hash(),
-                   "graph_replay_ms_per_step": graph_ms},
+                   "graph_replay_ms_per_step": graph_ms,
+                   "copy_GBps": copy_gbps,
+                   "frac_of_copy": ach / copy_gbps if copy_gbps else None},
     }
     if args.cpu_budget > 0:
         line["cpu_baseline"] = cpu_baseline(P, args.cpu_budget)
     print(json.dumps(line), flush=True)
+
+
+def copy_rate_gbps(mib: int = 1024, reps: int = 10):
+    """Bytes moved (read + write) per second by a plain device-to-device copy
+    of `mib` MiB, timed with events after the timed region: the rate that is
+    practically achievable for streaming reads and writes on this GPU."""
+    import torch
+    src = torch.ones(mib << 20, dtype=torch.uint8, device="cuda:0")
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(reps):
+        dst.copy_(src)
+    b.record()
+    torch.cuda.synchronize()
+    rate = 2 * src.numel() * reps / (a.elapsed_time(b) * 1e-3) / 1e9
+    del src, dst
+    return rate
 
 
 def graph_replay_ms(step, reps):
