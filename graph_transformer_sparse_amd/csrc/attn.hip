@@ -26,6 +26,8 @@
 // from the forward's log-sum-exp instead of storing U.
 #include <math.h>
 
+#include <stdlib.h>
+
 #include "device.hpp"
 #include "host.hpp"
 #include "layout.hpp"
@@ -41,6 +43,8 @@ struct Sched {
   const int32_t *items;  // [n_items][4]
   const int32_t *merges; // [n_merges][3]
   int64_t n_big, n_mid, n_small, n_items, n_merges;
+  int64_t block_base;    // workgroup offset of this launch (grids larger than one launch
+                         // allows go out in several launches)
 };
 
 // The segment a lane group works on.  wave_item: the whole wavefront shares
@@ -52,7 +56,7 @@ struct Work {
 
 template <int RPW>
 __device__ inline Work decode(const Sched &s, int grp) {
-  const int64_t w = (int64_t)blockIdx.x * WPB + threadIdx.x / WAVE;
+  const int64_t w = (s.block_base + blockIdx.x) * WPB + threadIdx.x / WAVE;
   Work k;
   k.active = true;
   if (w < s.n_items) {
@@ -434,7 +438,7 @@ template <typename T, int HL, int H>
 __global__ __launch_bounds__(BLOCK) void k_fwd_merge(FwdArgs a) {
   constexpr int N = Vec<T>::N, G = HL * H, D = G * N;
   const int lane = threadIdx.x & (WAVE - 1), grp = lane / G, gl = lane % G, h = gl / HL;
-  const int32_t *rec = a.s.merges + 3 * (int64_t)blockIdx.x;
+  const int32_t *rec = a.s.merges + 3 * (a.s.block_base + blockIdx.x);
   const int64_t row = rec[0], first = rec[1], nch = rec[2];
   FwdState<N> st;
   if (merge_pieces<FwdState<N>, D, H, G, fwd_slot_floats(D, H)>(st, a.part, first, nch,
@@ -577,7 +581,7 @@ template <typename T, int HL, int H>
 __global__ __launch_bounds__(BLOCK) void k_bwd_rows_merge(BwdArgs a) {
   constexpr int N = Vec<T>::N, G = HL * H, D = G * N;
   const int lane = threadIdx.x & (WAVE - 1), grp = lane / G, gl = lane % G, h = gl / HL;
-  const int32_t *rec = a.rows.merges + 3 * (int64_t)blockIdx.x;
+  const int32_t *rec = a.rows.merges + 3 * (a.rows.block_base + blockIdx.x);
   const int64_t row = rec[0], first = rec[1], nch = rec[2];
   RowState<N> st;
   if (merge_pieces<RowState<N>, D, H, G, rows_slot_floats(D, H)>(st, a.part_rows, first, nch,
@@ -688,7 +692,7 @@ template <typename T, int HL, int H>
 __global__ __launch_bounds__(BLOCK) void k_bwd_cols_merge(BwdArgs a) {
   constexpr int N = Vec<T>::N, G = HL * H, D = G * N;
   const int lane = threadIdx.x & (WAVE - 1), grp = lane / G, gl = lane % G, h = gl / HL;
-  const int32_t *rec = a.cols.merges + 3 * (int64_t)blockIdx.x;
+  const int32_t *rec = a.cols.merges + 3 * (a.cols.block_base + blockIdx.x);
   const int64_t col = rec[0], first = rec[1], nch = rec[2];
   ColState<N> st;
   if (merge_pieces<ColState<N>, D, H, G, cols_slot_floats(D, H)>(st, a.part_cols, first, nch,
@@ -705,21 +709,47 @@ static int64_t waves_for(const Sched &s, int rpw) {
   return s.n_items + s.n_mid + cdiv(s.n_small, rpw);
 }
 
+// At most 2^22 workgroups (2^30 work-items) per launch: a dispatch counts
+// its work-items in 32 bits.  Larger grids (only custom thresholds on
+// graphs of billions of nonzeros reach this) go out in several launches,
+// each told its workgroup offset.  GT_LAUNCH_BLOCKS (a positive integer)
+// lowers the limit, so that tests can take the several-launch path on
+// small graphs.
+static int64_t max_launch_blocks() {
+  constexpr int64_t LIMIT = (int64_t)1 << 22;
+  const char *e = getenv("GT_LAUNCH_BLOCKS");
+  if (e && *e) {
+    const long long v = atoll(e);
+    if (v > 0 && v < LIMIT) return v;
+  }
+  return LIMIT;
+}
+
+template <class Args, class Kernel>
+static void launch_blocks(Kernel kernel, Args a, Sched Args::*sched, int64_t nblocks,
+                          hipStream_t st) {
+  const int64_t lim = max_launch_blocks();
+  for (int64_t b0 = 0; b0 < nblocks; b0 += lim) {
+    (a.*sched).block_base = b0;
+    kernel<<<dim3((unsigned)std::min(lim, nblocks - b0)), BLOCK, 0, st>>>(a);
+  }
+}
+
 template <typename T, int HL, int H>
 static gt_status run_fwd(const FwdArgs &a, bool bias, hipStream_t st) {
   constexpr int G = HL * H, RPW = WAVE / G;
   const int64_t waves = waves_for(a.s, RPW);
   if (waves > 0) {
-    const dim3 grid((unsigned)cdiv(waves, WPB));
+    const int64_t nb = cdiv(waves, WPB);
     const int tok = prof_begin(PK_FWD, st);
-    if (bias) k_fwd<T, HL, H, UNROLL, true><<<grid, BLOCK, 0, st>>>(a);
-    else k_fwd<T, HL, H, UNROLL, false><<<grid, BLOCK, 0, st>>>(a);
+    if (bias) launch_blocks(k_fwd<T, HL, H, UNROLL, true>, a, &FwdArgs::s, nb, st);
+    else launch_blocks(k_fwd<T, HL, H, UNROLL, false>, a, &FwdArgs::s, nb, st);
     prof_end(tok, st);
     GT_CHECK_LAUNCH();
   }
   if (a.s.n_merges > 0) {
     const int tok = prof_begin(PK_FWD_MERGE, st);
-    k_fwd_merge<T, HL, H><<<dim3((unsigned)a.s.n_merges), BLOCK, 0, st>>>(a);
+    launch_blocks(k_fwd_merge<T, HL, H>, a, &FwdArgs::s, a.s.n_merges, st);
     prof_end(tok, st);
     GT_CHECK_LAUNCH();
   }
@@ -731,31 +761,31 @@ static gt_status run_bwd(const BwdArgs &a, bool bias, hipStream_t st) {
   constexpr int G = HL * H, RPW = WAVE / G;
   int64_t waves = waves_for(a.rows, RPW);
   if (waves > 0) {
-    const dim3 grid((unsigned)cdiv(waves, WPB));
+    const int64_t nb = cdiv(waves, WPB);
     const int tok = prof_begin(PK_BWD_ROWS, st);
-    if (bias) k_bwd_rows<T, HL, H, UNROLL, true><<<grid, BLOCK, 0, st>>>(a);
-    else k_bwd_rows<T, HL, H, UNROLL, false><<<grid, BLOCK, 0, st>>>(a);
+    if (bias) launch_blocks(k_bwd_rows<T, HL, H, UNROLL, true>, a, &BwdArgs::rows, nb, st);
+    else launch_blocks(k_bwd_rows<T, HL, H, UNROLL, false>, a, &BwdArgs::rows, nb, st);
     prof_end(tok, st);
     GT_CHECK_LAUNCH();
   }
   if (a.rows.n_merges > 0) {
     const int tok = prof_begin(PK_BWD_ROWS_MERGE, st);
-    k_bwd_rows_merge<T, HL, H><<<dim3((unsigned)a.rows.n_merges), BLOCK, 0, st>>>(a);
+    launch_blocks(k_bwd_rows_merge<T, HL, H>, a, &BwdArgs::rows, a.rows.n_merges, st);
     prof_end(tok, st);
     GT_CHECK_LAUNCH();
   }
   waves = waves_for(a.cols, RPW);
   if (waves > 0) {
-    const dim3 grid((unsigned)cdiv(waves, WPB));
+    const int64_t nb = cdiv(waves, WPB);
     const int tok = prof_begin(PK_BWD_COLS, st);
-    if (bias) k_bwd_cols<T, HL, H, UNROLL, true><<<grid, BLOCK, 0, st>>>(a);
-    else k_bwd_cols<T, HL, H, UNROLL, false><<<grid, BLOCK, 0, st>>>(a);
+    if (bias) launch_blocks(k_bwd_cols<T, HL, H, UNROLL, true>, a, &BwdArgs::cols, nb, st);
+    else launch_blocks(k_bwd_cols<T, HL, H, UNROLL, false>, a, &BwdArgs::cols, nb, st);
     prof_end(tok, st);
     GT_CHECK_LAUNCH();
   }
   if (a.cols.n_merges > 0) {
     const int tok = prof_begin(PK_BWD_COLS_MERGE, st);
-    k_bwd_cols_merge<T, HL, H><<<dim3((unsigned)a.cols.n_merges), BLOCK, 0, st>>>(a);
+    launch_blocks(k_bwd_cols_merge<T, HL, H>, a, &BwdArgs::cols, a.cols.n_merges, st);
     prof_end(tok, st);
     GT_CHECK_LAUNCH();
   }
@@ -828,6 +858,7 @@ static Sched sched_of(const gt_sched &s, const int32_t *ptr) {
   r.n_small = s.n_small;
   r.n_items = s.n_items;
   r.n_merges = s.n_merges;
+  r.block_base = 0;
   return r;
 }
 

@@ -11,8 +11,10 @@ the large outputs is still checked:
     edges, features and bias; only the order of each softmax sum differs).
     At n = 24 * 2^20, H = 4, dh = 32, bf16: Q, K, V, dY and the outputs hold
     3.2e9 elements (6.4 GB) each, the bias and dbias 2.4e9 (9.7 GB), and
-    nnz = 604M.  The transpose is checked bit-exactly against its closed
-    form (column j's sources are (j - o_k) mod n, ascending).
+    nnz = 604M; at n = 89.5M, H = 1, dh = 16: nnz = 2,147,483,136, just
+    below the int32 limit of the CSR.  The transpose is checked bit-exactly
+    against its closed form (column j's sources are (j - o_k) mod n,
+    ascending).
   * projections: X and the gradients periodic in the row (period P) at
     n = 2^24 + 2^18 rows of d = 128 (2.2e9 elements); Q, K, V, Z and dX are
     periodic, and dW = (n / P) times the oracle's product on one period.
@@ -155,13 +157,29 @@ def attention_case(n, deg, H, dh, seed, thresholds=None, device="cuda"):
     return n * D
 
 
+ATTN = {
+    # node arrays of 3.2e9 elements, bias of 2.4e9, nnz 604M
+    "elements": dict(n=24 << 20, deg=24, H=4, dh=32, gb=120),
+    # nnz = 2,147,483,136, just below the int32 limit of the CSR
+    "nnz": dict(n=1398101 * P, deg=24, H=1, dh=16, gb=140),
+}
+
+
 @pytest.mark.parametrize("th", [None, (8, 64, 64)], ids=["default", "wave_rows"])
-def test_attention_past_2_31_elements(th):
-    n, deg, H, dh = 24 << 20, 24, 4, 32
-    assert n * H * dh > 2 ** 31 and n * deg * H > 2 ** 31 and n * deg < 2 ** 31 - 1
+@pytest.mark.parametrize("case", list(ATTN))
+def test_attention_at_maximum_sizes(case, th):
+    """wave_rows makes every row a wavefront item: on the nnz case that is
+    89M wavefronts, a grid that has to go out in several launches."""
+    c = ATTN[case]
+    n, deg, H, dh = c["n"], c["deg"], c["H"], c["dh"]
+    assert n * deg < 2 ** 31 - 1
+    if case == "elements":
+        assert n * H * dh > 2 ** 31 and n * deg * H > 2 ** 31
+    else:
+        assert n * deg > 2 ** 31 - 2 ** 20
     free, _ = torch.cuda.mem_get_info()
-    if free < 120 << 30:
-        pytest.skip(f"needs about 120 GB of device memory, {free >> 30} GB free")
+    if free < c["gb"] << 30:
+        pytest.skip(f"needs about {c['gb']} GB of device memory, {free >> 30} GB free")
     try:
         attention_case(n, deg, H, dh, seed=31, thresholds=th)
     finally:

@@ -115,6 +115,26 @@ def test_bitwise_determinism():
             assert torch.equal(x, y) and torch.equal(x, z)
 
 
+@pytest.mark.parametrize("limit", ["1", "3"])
+def test_grid_in_several_launches(limit, monkeypatch):
+    """Grids larger than one launch allows go out in several launches, each
+    told its workgroup offset; GT_LAUNCH_BLOCKS lowers the limit so that a
+    small graph takes that path (every kernel and every merge in 1- or
+    3-workgroup launches).  Results are bitwise those of single launches."""
+    P = I.make_problem(I.CONFIGS["tiny"])
+    ip, ix = I.random_graph(21, 300, 280, _degrees(np.random.default_rng(21), 300, 280))
+    Pb = I.small_problem(21, ip, ix, 280, 4, 32, "bf16", True)
+    for prob, th in ((P, (2, 6, 4)), (Pb, (2, 8, 8)), (Pb, None)):
+        monkeypatch.delenv("GT_LAUNCH_BLOCKS", raising=False)
+        ref = run_gpu(prob, th)
+        monkeypatch.setenv("GT_LAUNCH_BLOCKS", limit)
+        got = run_gpu(prob, th)
+        for x, y in zip(ref, got):
+            if x is not None:
+                assert torch.equal(x, y)
+        check_full(prob, got)
+
+
 def test_autograd_function_matches_abi():
     ip, ix = I.random_graph(11, 80, 80, np.random.default_rng(1).integers(1, 40, 80))
     P = I.small_problem(11, ip, ix, 80, 4, 32, "bf16", True)
