@@ -26,6 +26,7 @@ the ALUs; s = bytes per element, D = H*dh, b = 1 with a per-edge bias):
 from __future__ import annotations
 
 import argparse
+import dataclasses
 import hashlib
 import json
 import os
@@ -175,6 +176,10 @@ def main():
                     help="time the head repack of graph parallelism with all-to-all for P "
                          "workers (split of Q, K, V and merge of Y) and the attention run on "
                          "the P head slices, instead of the plain attention step")
+    ap.add_argument("--hidden", type=int, default=0, metavar="D",
+                    help="run the workload's graph and head count at hidden size D (head_dim = "
+                         "D / heads) instead of its own; the pages vary the hidden size over 64, "
+                         "128 and 256 at 8 heads (Section 5.4, Figure 7)")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
                     help="only run a plain device-to-device copy of MIB MiB, 5 times "
                          "(calibrates the HBM byte counters against a known size)")
@@ -201,6 +206,11 @@ def main():
 
     T.lib()
     cfg = I.CONFIGS[args.config]
+    if args.hidden:
+        if args.hidden % cfg.heads:
+            sys.exit(f"--hidden {args.hidden} is not a multiple of the {cfg.heads} heads")
+        cfg = dataclasses.replace(cfg, head_dim=args.hidden // cfg.heads,
+                                  desc=f"{cfg.desc}; hidden {args.hidden}")
     if args.layer:
         return layer_bench(args, cfg)
     if args.head_split:
@@ -276,7 +286,8 @@ def main():
             kern[k]["model_GB"] = model[k] / 1e9
             kern[k]["GBps"] = model[k] / (kern[k]["ms_per_launch"] * 1e-3) / 1e9
     ach = kern[dominant]["GBps"]
-    traffic = traffic_record(dominant, cfg.name)
+    # the committed counter records are for each workload's own shape
+    traffic = None if args.hidden else traffic_record(dominant, cfg.name)
     total_model = sum(model.values())
     graph_ms = graph_replay_ms(step, args.steps)
     copy_gbps = copy_rate_gbps()
@@ -511,7 +522,7 @@ def layer_bench(args, cfg):
                    "bias": cfg.bias, "parallelism": "single GPU"},
         "roofline": {"bound": "hbm", "kernel": dominant, "achieved": ach, "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": ach / HBM_PEAK_GBS,
-                     "traffic": traffic_record(dominant, cfg.name)},
+                     "traffic": None if args.hidden else traffic_record(dominant, cfg.name)},
         "cpu_baseline": None,
         "detail": {"kernels": kern, "input_gen_s": gen_s,
                    "kernel_source_hash": kernel_source_hash()},

@@ -807,17 +807,22 @@ static bool by_heads(int heads, F &&f) {
 
 template <typename F>
 static bool dispatch(gt_dtype dt, int heads, int head_dim, F &&f) {
+  // HL = head_dim * sizeof(T) / 16 lanes per head
   if (dt == GT_F32) {
     switch (head_dim) {
+      case 8: return by_heads<float, 2>(heads, f);
       case 16: return by_heads<float, 4>(heads, f);
       case 32: return by_heads<float, 8>(heads, f);
       case 64: return by_heads<float, 16>(heads, f);
+      case 128: return by_heads<float, 32>(heads, f);
     }
   } else if (dt == GT_BF16) {
     switch (head_dim) {
+      case 8: return by_heads<bf16_t, 1>(heads, f);
       case 16: return by_heads<bf16_t, 2>(heads, f);
       case 32: return by_heads<bf16_t, 4>(heads, f);
       case 64: return by_heads<bf16_t, 8>(heads, f);
+      case 128: return by_heads<bf16_t, 16>(heads, f);
     }
   }
   return false;

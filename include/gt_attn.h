@@ -42,9 +42,10 @@
  *     them into a HIP graph and replay it.
  *   - Dense features are row-major [n, heads, head_dim] (node-major, heads
  *     contiguous), in the dtype `dt`; rows start 16-byte aligned.
- *     Supported: head_dim in {16, 32, 64}, heads in {1, 2, 4, 8}, and
- *     heads * head_dim * sizeof(dt) <= 1024 bytes (a row fits one wavefront
- *     at 16 bytes a lane).  Softmax statistics (lse),
+ *     Supported: head_dim in {8, 16, 32, 64, 128}, heads in {1, 2, 4, 8},
+ *     and heads * head_dim * sizeof(dt) <= 1024 bytes (a row fits one
+ *     wavefront at 16 bytes a lane).  head_dim 8 is the paper's hidden
+ *     size 64 over 8 heads (Section 5.4, Figure 7).  Softmax statistics (lse),
  *     bias and dbias are float32.  All arithmetic is float32; bf16 inputs
  *     are widened exactly and bf16 outputs are rounded to nearest even.
  *   - CSR: indptr[n_rows + 1], indices[nnz], int32, columns strictly

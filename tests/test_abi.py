@@ -72,6 +72,9 @@ def test_fwd_argument_checks(L):
     assert _fwd(L, g, dh=48) == 4                   # head_dim
     assert _fwd(L, g, heads=3) == 4                 # heads
     assert _fwd(L, g, heads=8, dh=64) == 4          # 2 KiB rows in fp32
+    assert _fwd(L, g, heads=4, dh=128) == 4         # 2 KiB rows in fp32
+    assert _fwd(L, g, dh=256) == 4                  # head_dim
+    assert _fwd(L, g, dh=4) == 4                    # head_dim
     assert _fwd(L, g, Q=None) == 1
     assert _fwd(L, g, K=ODD) == 5
     assert _fwd(L, g, lse=None) == 1

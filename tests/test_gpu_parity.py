@@ -60,6 +60,9 @@ SHAPES = [  # dtype, heads, head_dim
     ("f32", 1, 64), ("f32", 8, 16), ("f32", 2, 32), ("f32", 4, 64), ("f32", 8, 32),
     ("bf16", 8, 32), ("bf16", 4, 32), ("bf16", 8, 16), ("bf16", 1, 16), ("bf16", 8, 64),
     ("bf16", 2, 64), ("f32", 1, 16),
+    # hidden 64 over 8 heads (the paper's smallest hidden size, Figure 7), and head_dim 128
+    ("f32", 8, 8), ("bf16", 8, 8), ("bf16", 1, 8), ("f32", 2, 128), ("bf16", 4, 128),
+    ("bf16", 1, 128),
 ]
 THRESH = [None, (2, 8, 8), (4, 16, 5), (0, 0, 3)]
 

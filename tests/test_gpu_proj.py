@@ -68,7 +68,8 @@ def test_weight_gradient_is_deterministic():
         assert torch.equal(x, y)
 
 
-LAYER = [("f32", 2, 32, False), ("bf16", 4, 32, True), ("f32", 1, 64, True), ("bf16", 8, 32, False)]
+LAYER = [("f32", 2, 32, False), ("bf16", 4, 32, True), ("f32", 1, 64, True), ("bf16", 8, 32, False),
+         ("bf16", 8, 8, True)]   # the last: hidden 64 over 8 heads (Figure 7)
 
 
 @pytest.mark.parametrize("case", LAYER, ids=[f"{a}-h{b}-d{c}-{'bias' if e else 'nobias'}" for a, b, c, e in LAYER])
