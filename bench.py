@@ -90,9 +90,45 @@ def traffic_record(kernel: str, workload: str):
         return None
 
 
-def cpu_baseline(P, budget_s: float):
+RTOL = {"f32": 1e-5, "bf16": 2e-2}
+U32 = 2.0 ** -24
+
+
+def _compare(got, ref, rtol, mag=None, head_axis=1):
+    """Relative L2 error per head (the largest) and the largest elementwise
+    error over its bound rtol |r| + rtol rms(r) + 8 u mag (mag: the oracle's
+    sum of the absolute values of the terms of each element)."""
+    axes = tuple(a for a in range(ref.ndim) if a != head_axis)
+    rms = np.sqrt(np.mean(ref ** 2, axis=axes, keepdims=True))
+    r2 = np.sqrt(np.sum(ref ** 2, axis=axes))
+    d2 = np.sqrt(np.sum((got - ref) ** 2, axis=axes))
+    rel = float(np.max(np.where(r2 > 0, d2 / np.maximum(r2, 1e-300), 0.0)))
+    bound = rtol * np.abs(ref) + rtol * rms
+    if mag is not None:
+        bound = bound + 8 * U32 * mag
+    err = np.abs(got - ref)
+    ratio = float(np.max(np.where(err > 0, err / np.maximum(bound, 1e-300), 0.0)))
+    return {"rel_l2": rel, "max_err_over_bound": ratio, "ok": bool(rel <= rtol and ratio <= 1.0)}
+
+
+def _compare_lse(got, ref, rtol):
+    ninf = np.isneginf(ref)
+    same = bool(np.array_equal(np.isneginf(got), ninf))
+    f = ~ninf
+    ratio = float(np.max(np.abs(got[f] - ref[f]) / (rtol * np.maximum(1.0, np.abs(ref[f])))))\
+        if f.any() else 0.0
+    return {"max_err_over_bound": ratio, "ok": bool(same and ratio <= 1.0)}
+
+
+def cpu_baseline(P, budget_s: float, gpu_rows=None):
     """The oracle (fp64, OpenMP) on a row block of the same workload whose
-    size is picked so the run takes about budget_s seconds."""
+    size is picked so the run takes about budget_s seconds.
+
+    gpu_rows(k, e), if given, returns the GPU's outputs of the timed run for
+    the first k rows (Y, lse, dQ, and dbias of their e edges; dK and dV when
+    k covers every row); they are compared with the oracle's outputs on the
+    same block, at the tolerance of the parity tests, and the verdict is
+    reported beside the timing."""
     from oracle import oracle as O
     cfg = P.cfg
     # the oracle works in float64: widen the inputs once, outside the timing
@@ -105,12 +141,14 @@ def cpu_baseline(P, budget_s: float):
         e = int(ip[-1])
         return ip, P.indices[:e], (B[:e] if B is not None else None), e
 
-    def run(k):
+    def run(k, mag=None):
         ip, ix, bias, e = block(k)
         q, dy = np.ascontiguousarray(Q[:k]), np.ascontiguousarray(dY[:k])
         t = time.perf_counter()
-        O.fwd(ip, ix, cfg.n_cols, q, K, V, bias, P.scale)
-        O.bwd(ip, ix, cfg.n_cols, q, K, V, dy, bias, P.scale)
+        out = O.fwd(ip, ix, cfg.n_cols, q, K, V, bias, P.scale, mag=mag)
+        out += O.bwd(ip, ix, cfg.n_cols, q, K, V, dy, bias, P.scale, mag=mag)
+        if mag is not None:
+            return out
         return time.perf_counter() - t, e
 
     def sized(budget):
@@ -146,7 +184,31 @@ def cpu_baseline(P, budget_s: float):
         O.set_threads(cores)
     out["single_thread"] = {"value": e1 * runs1 / total1 / 1e9, "unit": "GEdges/s",
                             "sample": f"rows 0..{k1 - 1}, {runs1} run(s) in {total1:.1f} s"}
+    if gpu_rows is not None:
+        out["parity"] = parity_on_block(P, k, e, run, gpu_rows)
     return out
+
+
+def parity_on_block(P, k, e, run, gpu_rows):
+    """The oracle's outputs on rows 0..k-1 (one more, untimed run that also
+    returns the magnitudes of the sums) against the GPU's outputs there."""
+    cfg, rtol = P.cfg, RTOL[P.cfg.dtype]
+    mag = {}
+    Y, lse, dQ, dK, dV, dB = run(k, mag)
+    g = gpu_rows(k, e)
+    rep = {"Y": _compare(g["Y"], Y, rtol, mag["Y"]), "lse": _compare_lse(g["lse"], lse, rtol),
+           "dQ": _compare(g["dQ"], dQ, rtol, mag["dQ"])}
+    if dB is not None:
+        rep["dbias"] = _compare(g["dbias"], dB, rtol)
+    if k == cfg.n_rows:
+        rep["dK"] = _compare(g["dK"], dK, rtol, mag["dK"])
+        rep["dV"] = _compare(g["dV"], dV, rtol, mag["dV"])
+    what = "Y, lse, dQ" + (", dbias" if dB is not None else "")
+    what += ", dK, dV (every row in the block)" if k == cfg.n_rows else \
+        " (dK, dV need every row; compared by the tests)"
+    return {"verdict": "pass" if all(r["ok"] for r in rep.values()) else "FAIL",
+            "rtol": rtol, "compared": f"{what} of rows 0..{k - 1} from the timed run",
+            "tensors": rep}
 
 
 def cpu_model() -> str:
@@ -325,7 +387,18 @@ def main():
                    "frac_of_copy": ach / copy_gbps if copy_gbps else None},
     }
     if args.cpu_budget > 0:
-        line["cpu_baseline"] = cpu_baseline(P, args.cpu_budget)
+        def gpu_rows(k, e):
+            f64 = lambda t: t.float().cpu().numpy().astype(np.float64)
+            out = {"Y": f64(Y[:k]), "lse": f64(lse[:k]), "dQ": f64(dQ[:k])}
+            if dbias is not None:
+                out["dbias"] = f64(dbias[:e])
+            if k == R:
+                out["dK"], out["dV"] = f64(dK), f64(dV)
+            return out
+        line["cpu_baseline"] = cpu_baseline(P, args.cpu_budget, gpu_rows)
+        if line["cpu_baseline"]["parity"]["verdict"] != "pass":
+            print("bench: the GPU outputs of the timed run do NOT match the oracle",
+                  file=sys.stderr)
     print(json.dumps(line), flush=True)
 
 
