@@ -121,6 +121,44 @@ def _dt(dtype) -> int:
     raise TypeError(f"unsupported dtype {dtype}")
 
 
+def _need(cond: bool, where: str, msg: str):
+    if not cond:
+        raise ValueError(f"{where}: {msg}")
+
+
+def _tensor(where: str, name: str, t, shape, dtype, device):
+    """Check that t is a contiguous tensor of this shape, dtype and device.
+    The C ABI gets only pointers: a wrongly sized array would be read or
+    written out of bounds on the GPU, so sizes are checked here."""
+    _need(isinstance(t, torch.Tensor), where, f"{name} must be a tensor")
+    _need(tuple(t.shape) == tuple(shape), where,
+          f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    _need(t.dtype == dtype, where, f"{name} has dtype {t.dtype}, expected {dtype}")
+    _need(t.device == device, where, f"{name} is on {t.device}, expected {device}")
+    _need(t.is_contiguous(), where, f"{name} must be contiguous")
+
+
+def _attn_shapes(where: str, g: "Graph", Q, K, V, bias):
+    """(R, H, dh, dtype, device) of the attention inputs, checked against the
+    prepared graph."""
+    _need(isinstance(Q, torch.Tensor) and Q.dim() == 3, where, "Q must be a [rows, heads, "
+          "head_dim] tensor")
+    R, H, dh = Q.shape
+    dt, dev = Q.dtype, Q.device
+    _need(dt in (torch.float32, torch.bfloat16), where, f"unsupported dtype {dt}")
+    _tensor(where, "Q", Q, (g.n_rows, H, dh), dt, dev)
+    _tensor(where, "K", K, (g.n_cols, H, dh), dt, dev)
+    _tensor(where, "V", V, (g.n_cols, H, dh), dt, dev)
+    if bias is not None:
+        _tensor(where, "bias", bias, (g.nnz, H), torch.float32, dev)
+    return R, H, dh, dt, dev
+
+
+def _on_gpu(where: str, g: "Graph", dev):
+    _need(dev.type == "cuda", where, f"tensors must be on a GPU, not {dev}")
+    _need(g.meta.device == dev, where, f"the graph is on {g.meta.device}, the tensors on {dev}")
+
+
 def gt_default_thresholds():
     a, b, c = _i32(), _i32(), _i32()
     lib().gt_default_thresholds(C.byref(a), C.byref(b), C.byref(c))
@@ -154,7 +192,8 @@ class Graph:
     def _view(self, ptr: int, n: int) -> torch.Tensor:
         base = self.meta.data_ptr()
         off = ptr - base
-        assert off % 4 == 0 and 0 <= off and off + 4 * n <= self.meta.numel()
+        if off % 4 or off < 0 or off + 4 * n > self.meta.numel():
+            raise RuntimeError("graph struct points outside its meta buffer")
         return self.meta.view(torch.int32)[off // 4: off // 4 + n]
 
     @property
@@ -202,8 +241,14 @@ def gt_graph_prepare(indptr: torch.Tensor, indices: torch.Tensor, n_cols: int,
     t_small = d_small if t_small is None else t_small
     t_mid = d_mid if t_mid is None else t_mid
     chunk = d_chunk if chunk is None else chunk
-    assert indptr.dtype == torch.int32 and indices.dtype == torch.int32
-    assert indptr.is_contiguous() and indices.is_contiguous()
+    where = "gt_graph_prepare"
+    for name, t in (("indptr", indptr), ("indices", indices)):
+        _need(isinstance(t, torch.Tensor) and t.dim() == 1, where, f"{name} must be a 1-D tensor")
+        _need(t.dtype == torch.int32, where, f"{name} must be int32, not {t.dtype}")
+        _need(t.is_contiguous(), where, f"{name} must be contiguous")
+    _need(indptr.numel() >= 1, where, "indptr needs n_rows + 1 >= 1 entries")
+    _need(indptr.device.type == "cuda" and indices.device == indptr.device, where,
+          "indptr and indices must be on the same GPU")
     R, E = indptr.numel() - 1, indices.numel()
     nb = L.gt_graph_meta_bytes(R, n_cols, E, chunk)
     if nb == 0:
@@ -234,6 +279,9 @@ def gt_attn_work_bytes(g: Graph, heads: int, head_dim: int) -> int:
 
 def _work(g, heads, head_dim, device, work):
     nb = gt_attn_work_bytes(g, heads, head_dim)
+    if work is not None:
+        _need(work.dtype == torch.uint8 and work.device == device and work.is_contiguous(),
+              "work", "work must be a contiguous uint8 tensor on the inputs' device")
     if work is None or work.numel() < nb:
         work = torch.empty(nb, dtype=torch.uint8, device=device)
     return work
@@ -241,15 +289,14 @@ def _work(g, heads, head_dim, device, work):
 
 def gt_attn_fwd(g: Graph, Q, K, V, bias=None, scale=None, work=None, Y=None, lse=None):
     """Forward: returns (Y, lse).  Q [R,H,dh], K/V [M,H,dh] (f32 or bf16)."""
-    R, H, dh = Q.shape
+    R, H, dh, dt, dev = _attn_shapes("gt_attn_fwd", g, Q, K, V, bias)
     scale = dh ** -0.5 if scale is None else float(scale)
-    for t in (Q, K, V):
-        assert t.is_contiguous() and t.dtype == Q.dtype
-    if bias is not None:
-        assert bias.dtype == torch.float32 and bias.is_contiguous()
     Y = torch.empty_like(Q) if Y is None else Y
-    lse = torch.empty((R, H), dtype=torch.float32, device=Q.device) if lse is None else lse
-    work = _work(g, H, dh, Q.device, work)
+    lse = torch.empty((R, H), dtype=torch.float32, device=dev) if lse is None else lse
+    _tensor("gt_attn_fwd", "Y", Y, (R, H, dh), dt, dev)
+    _tensor("gt_attn_fwd", "lse", lse, (R, H), torch.float32, dev)
+    _on_gpu("gt_attn_fwd", g, dev)
+    work = _work(g, H, dh, dev, work)
     _check(lib().gt_attn_fwd(C.byref(g.st), H, dh, _dt(Q.dtype), scale, _ptr(Q), _ptr(K),
                              _ptr(V), _ptr(bias), _ptr(Y), _ptr(lse), _ptr(work),
                              work.numel(), _stream(Q.device)), "gt_attn_fwd")
@@ -259,16 +306,24 @@ def gt_attn_fwd(g: Graph, Q, K, V, bias=None, scale=None, work=None, Y=None, lse
 def gt_attn_bwd(g: Graph, Q, K, V, lse, dY, bias=None, scale=None, work=None,
                 dQ=None, dK=None, dV=None, dbias=None):
     """Backward: returns (dQ, dK, dV, dbias); dbias is None without bias."""
-    R, H, dh = Q.shape
+    where = "gt_attn_bwd"
+    R, H, dh, dt, dev = _attn_shapes(where, g, Q, K, V, bias)
     scale = dh ** -0.5 if scale is None else float(scale)
-    for t in (Q, K, V, dY):
-        assert t.is_contiguous() and t.dtype == Q.dtype
+    _tensor(where, "lse", lse, (R, H), torch.float32, dev)
+    _tensor(where, "dY", dY, (R, H, dh), dt, dev)
     dQ = torch.empty_like(Q) if dQ is None else dQ
     dK = torch.empty_like(K) if dK is None else dK
     dV = torch.empty_like(V) if dV is None else dV
     if bias is not None and dbias is None:
         dbias = torch.empty_like(bias)
-    work = _work(g, H, dh, Q.device, work)
+    _need((bias is None) == (dbias is None), where, "bias and dbias go together")
+    _tensor(where, "dQ", dQ, (R, H, dh), dt, dev)
+    _tensor(where, "dK", dK, (g.n_cols, H, dh), dt, dev)
+    _tensor(where, "dV", dV, (g.n_cols, H, dh), dt, dev)
+    if dbias is not None:
+        _tensor(where, "dbias", dbias, (g.nnz, H), torch.float32, dev)
+    _on_gpu(where, g, dev)
+    work = _work(g, H, dh, dev, work)
     _check(lib().gt_attn_bwd(C.byref(g.st), H, dh, _dt(Q.dtype), scale, _ptr(Q), _ptr(K),
                              _ptr(V), _ptr(bias), _ptr(lse), _ptr(dY), _ptr(dQ),
                              _ptr(dK), _ptr(dV), _ptr(dbias), _ptr(work), work.numel(),
@@ -349,14 +404,25 @@ def _proj_lib():
     return L
 
 
-def _nd(X):
-    assert X.dim() == 2 and X.is_contiguous()
-    return X.shape[0], X.shape[1]
+def _nd(where: str, X, *others):
+    """(n, d) of X [n, d]; `others` are (name, tensor, shape) to check against it."""
+    _need(isinstance(X, torch.Tensor) and X.dim() == 2, where, "X must be a [n, d] tensor")
+    _need(X.dtype in (torch.float32, torch.bfloat16), where, f"unsupported dtype {X.dtype}")
+    _need(X.is_contiguous(), where, "X must be contiguous")
+    n, d = X.shape
+    for name, t, shape in others:
+        _tensor(where, name, t, shape(n, d), X.dtype, X.device)
+    _need(X.device.type == "cuda", where, f"tensors must be on a GPU, X is on {X.device}")
+    return n, d
+
+
+_W = lambda n, d: (d, d)
+_ND = lambda n, d: (n, d)
 
 
 def gt_proj_qkv(X, Wq, Wk, Wv):
     """Q, K, V = X W_q, X W_k, X W_v; X [n, d], W [d, d] (f32 or bf16)."""
-    n, d = _nd(X)
+    n, d = _nd("gt_proj_qkv", X, ("Wq", Wq, _W), ("Wk", Wk, _W), ("Wv", Wv, _W))
     Q, K, V = (torch.empty_like(X) for _ in range(3))
     _check(_proj_lib().gt_proj_qkv(n, d, _dt(X.dtype), _ptr(X), _ptr(Wq), _ptr(Wk), _ptr(Wv),
                                    _ptr(Q), _ptr(K), _ptr(V), _stream(X.device)), "gt_proj_qkv")
@@ -365,7 +431,7 @@ def gt_proj_qkv(X, Wq, Wk, Wv):
 
 def gt_proj_out(X, Wo, Y):
     """Z = X W_o + Y."""
-    n, d = _nd(X)
+    n, d = _nd("gt_proj_out", X, ("Wo", Wo, _W), ("Y", Y, _ND))
     Z = torch.empty_like(X)
     _check(_proj_lib().gt_proj_out(n, d, _dt(X.dtype), _ptr(X), _ptr(Wo), _ptr(Y), _ptr(Z),
                                    _stream(X.device)), "gt_proj_out")
@@ -374,7 +440,8 @@ def gt_proj_out(X, Wo, Y):
 
 def gt_proj_bwd_data(dZ, dQ, dK, dV, Wo, Wq, Wk, Wv):
     """dX = dZ W_o^T + dQ W_q^T + dK W_k^T + dV W_v^T."""
-    n, d = _nd(dZ)
+    n, d = _nd("gt_proj_bwd_data", dZ, ("dQ", dQ, _ND), ("dK", dK, _ND), ("dV", dV, _ND),
+               ("Wo", Wo, _W), ("Wq", Wq, _W), ("Wk", Wk, _W), ("Wv", Wv, _W))
     dX = torch.empty_like(dZ)
     _check(_proj_lib().gt_proj_bwd_data(n, d, _dt(dZ.dtype), _ptr(dZ), _ptr(dQ), _ptr(dK),
                                         _ptr(dV), _ptr(Wo), _ptr(Wq), _ptr(Wk), _ptr(Wv),
@@ -384,9 +451,13 @@ def gt_proj_bwd_data(dZ, dQ, dK, dV, Wo, Wq, Wk, Wv):
 
 def gt_proj_bwd_weight(X, dZ, dQ, dK, dV, work=None):
     """dW_o, dW_q, dW_k, dW_v = X^T dZ, X^T dQ, X^T dK, X^T dV (float32)."""
-    n, d = _nd(X)
+    n, d = _nd("gt_proj_bwd_weight", X, ("dZ", dZ, _ND), ("dQ", dQ, _ND), ("dK", dK, _ND),
+               ("dV", dV, _ND))
     L = _proj_lib()
     nb = L.gt_proj_work_bytes(n, d)
+    if work is not None:
+        _need(work.dtype == torch.uint8 and work.device == X.device and work.is_contiguous(),
+              "gt_proj_bwd_weight", "work must be a contiguous uint8 tensor on X's device")
     if work is None or work.numel() < nb:
         work = torch.empty(nb, dtype=torch.uint8, device=X.device)
     dW = [torch.empty((d, d), dtype=torch.float32, device=X.device) for _ in range(4)]
@@ -440,7 +511,9 @@ def sga_layer(g: Graph, heads: int, X, Wq, Wk, Wv, Wo, bias=None, scale=None):
 
 def _heads_geometry(t: torch.Tensor):
     """(rows, heads, head_bytes) of a contiguous [rows, heads, ...] tensor."""
-    assert t.is_contiguous() and t.dim() >= 2
+    _need(isinstance(t, torch.Tensor) and t.dim() >= 2 and t.is_contiguous(), "head repack",
+          "expects a contiguous [rows, heads, ...] tensor")
+    _need(t.device.type == "cuda", "head repack", f"tensors must be on a GPU, not {t.device}")
     rows, heads = t.shape[0], t.shape[1]
     per_head = t[0, 0].numel() if rows > 0 else math.prod(t.shape[2:])
     return rows, heads, int(per_head) * t.element_size()
@@ -450,8 +523,11 @@ def gt_head_split(x: torch.Tensor, parts: int, out=None) -> torch.Tensor:
     """[rows, heads, ...] -> [parts, rows, heads/parts, ...]: part r holds
     heads r*heads/parts .. (r+1)*heads/parts - 1 of every row."""
     rows, heads, hb = _heads_geometry(x)
+    _need(parts >= 1 and heads % parts == 0, "gt_head_split",
+          f"{heads} heads do not split into {parts} equal parts")
     shape = (parts, rows, heads // parts) + tuple(x.shape[2:])
     out = torch.empty(shape, dtype=x.dtype, device=x.device) if out is None else out
+    _tensor("gt_head_split", "out", out, shape, x.dtype, x.device)
     _check(lib().gt_head_split(rows, heads, hb, parts, _ptr(x), _ptr(out), _stream(x.device)),
            "gt_head_split")
     return out
@@ -459,12 +535,15 @@ def gt_head_split(x: torch.Tensor, parts: int, out=None) -> torch.Tensor:
 
 def gt_head_merge(p: torch.Tensor, out=None) -> torch.Tensor:
     """The inverse of gt_head_split: [parts, rows, hp, ...] -> [rows, parts*hp, ...]."""
-    assert p.is_contiguous() and p.dim() >= 3
+    _need(isinstance(p, torch.Tensor) and p.dim() >= 3 and p.is_contiguous(), "gt_head_merge",
+          "expects a contiguous [parts, rows, heads/parts, ...] tensor")
+    _need(p.device.type == "cuda", "gt_head_merge", f"tensors must be on a GPU, not {p.device}")
     parts, rows, hp = p.shape[0], p.shape[1], p.shape[2]
     heads = parts * hp
     hb = math.prod(p.shape[3:]) * p.element_size()
     shape = (rows, heads) + tuple(p.shape[3:])
     out = torch.empty(shape, dtype=p.dtype, device=p.device) if out is None else out
+    _tensor("gt_head_merge", "out", out, shape, p.dtype, p.device)
     _check(lib().gt_head_merge(rows, heads, hb, parts, _ptr(p), _ptr(out), _stream(p.device)),
            "gt_head_merge")
     return out

@@ -59,7 +59,7 @@ def test_unaligned_and_empty():
 
 def test_split_rejects_bad_shapes():
     x = torch.zeros((4, 6, 16), device="cuda")
-    with pytest.raises(T.GTError):
+    with pytest.raises(ValueError):
         T.gt_head_split(x, 4)                   # 6 heads do not divide among 4 workers
 
 
