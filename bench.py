@@ -242,6 +242,10 @@ def main():
                     help="run the workload's graph and head count at hidden size D (head_dim = "
                          "D / heads) instead of its own; the pages vary the hidden size over 64, "
                          "128 and 256 at 8 heads (Section 5.4, Figure 7)")
+    ap.add_argument("--nodes", type=int, default=0, metavar="N",
+                    help="mid only: the same R-MAT recipe on N nodes (a power of two); the "
+                         "pages compare sparse graph attention at 64K, 128K and 512K nodes "
+                         "(Section 5.4, Figure 6)")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
                     help="only run a plain device-to-device copy of MIB MiB, 5 times "
                          "(calibrates the HBM byte counters against a known size)")
@@ -268,6 +272,11 @@ def main():
 
     T.lib()
     cfg = I.CONFIGS[args.config]
+    if args.nodes:
+        if cfg.name != "mid" or args.nodes < 2 or args.nodes & (args.nodes - 1):
+            sys.exit("--nodes takes a power of two, with the mid workload")
+        cfg = dataclasses.replace(cfg, n_rows=args.nodes, n_cols=args.nodes,
+                                  desc=f"{cfg.desc}; {args.nodes} nodes")
     if args.hidden:
         if args.hidden % cfg.heads:
             sys.exit(f"--hidden {args.hidden} is not a multiple of the {cfg.heads} heads")
@@ -317,6 +326,18 @@ def main():
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
+    # device memory a step allocates beyond the resident inputs, outputs and
+    # buffers (the library allocates nothing: expected 0)
+    torch.cuda.reset_peak_memory_stats()
+    base = torch.cuda.memory_allocated()
+    step()
+    torch.cuda.synchronize()
+    memory = {"step_allocates_bytes": torch.cuda.max_memory_allocated() - base,
+              "meta_bytes": g.meta.numel(), "work_bytes": work.numel(),
+              # what the forward leaves for the backward besides its inputs and Y
+              "saved_fwd_to_bwd_bytes": lse.numel() * lse.element_size(),
+              # the same kept as one float32 attention weight per edge and head
+              "per_edge_weights_bytes": E * H * 4}
     # three more untimed steps with every kernel timed: per-kernel times and
     # the dominant kernel
     T.prof_reset()
@@ -348,8 +369,8 @@ def main():
             kern[k]["model_GB"] = model[k] / 1e9
             kern[k]["GBps"] = model[k] / (kern[k]["ms_per_launch"] * 1e-3) / 1e9
     ach = kern[dominant]["GBps"]
-    # the committed counter records are for each workload's own shape
-    traffic = None if args.hidden else traffic_record(dominant, cfg.name)
+    # the committed counter records are for each workload's own shape and size
+    traffic = None if (args.hidden or args.nodes) else traffic_record(dominant, cfg.name)
     total_model = sum(model.values())
     graph_ms = graph_replay_ms(step, args.steps)
     copy_gbps = copy_rate_gbps()
@@ -380,7 +401,8 @@ def main():
                    "step_ms_events": {"mean": sum(per_step) / len(per_step),
                                       "min": per_step[0],
                                       "median": per_step[len(per_step) // 2]},
-                   "kernels": kern, "prep_ms": prep_ms, "input_gen_s": gen_s,
+                   "kernels": kern, "memory": memory, "prep_ms": prep_ms,
+                   "input_gen_s": gen_s,
                    "kernel_source_hash": kernel_source_hash(),
                    "graph_replay_ms_per_step": graph_ms,
                    "copy_GBps": copy_gbps,
@@ -595,7 +617,8 @@ def layer_bench(args, cfg):
                    "bias": cfg.bias, "parallelism": "single GPU"},
         "roofline": {"bound": "hbm", "kernel": dominant, "achieved": ach, "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": ach / HBM_PEAK_GBS,
-                     "traffic": None if args.hidden else traffic_record(dominant, cfg.name)},
+                     "traffic": (None if (args.hidden or args.nodes)
+                                 else traffic_record(dominant, cfg.name))},
         "cpu_baseline": None,
         "detail": {"kernels": kern, "input_gen_s": gen_s,
                    "kernel_source_hash": kernel_source_hash()},

@@ -122,7 +122,7 @@ gt_status check_common(const gt_graph *g, int heads, int head_dim, gt_dtype dt) 
   if (g->n_rows < 0 || g->n_cols < 0 || g->nnz < 0)
     return fail(GT_E_ARG, "graph has negative sizes");
   if (!g->indptr || (g->nnz > 0 && !g->indices) || !g->indptr_t || !g->rows.order ||
-      !g->cols.order)
+      !g->cols.order || !g->rows.spans || !g->cols.spans)
     return fail(GT_E_NULL, "graph is not prepared");
   return GT_OK;
 }

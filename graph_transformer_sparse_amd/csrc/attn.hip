@@ -38,10 +38,10 @@ constexpr int BLOCK = 256;
 constexpr int WPB = BLOCK / WAVE;
 
 struct Sched {
-  const int32_t *ptr;    // [n_seg + 1] segment pointer (indptr or indptr_t)
   const int32_t *order;  // degree order
   const int32_t *items;  // [n_items][4]
   const int32_t *merges; // [n_merges][3]
+  const int32_t *spans;  // [n_seg][2] extent of each segment of `order`
   int64_t n_big, n_mid, n_small, n_items, n_merges;
   int64_t block_base;    // workgroup offset of this launch (grids larger than one launch
                          // allows go out in several launches)
@@ -67,9 +67,11 @@ __device__ inline Work decode(const Sched &s, int grp) {
     k.slot = it.w;
     k.wave_item = true;
   } else if (w < s.n_items + s.n_mid) {
-    k.seg = s.order[s.n_big + (w - s.n_items)];
-    k.eb = s.ptr[k.seg];
-    k.ee = s.ptr[k.seg + 1];
+    const int64_t o = s.n_big + (w - s.n_items);
+    k.seg = s.order[o];
+    const int2 sp = *reinterpret_cast<const int2 *>(s.spans + 2 * o);
+    k.eb = sp.x;
+    k.ee = sp.y;
     k.slot = -1;
     k.wave_item = true;
   } else {
@@ -81,9 +83,11 @@ __device__ inline Work decode(const Sched &s, int grp) {
       k.seg = 0;
       k.eb = k.ee = 0;
     } else {
-      k.seg = s.order[s.n_big + s.n_mid + q];
-      k.eb = s.ptr[k.seg];
-      k.ee = s.ptr[k.seg + 1];
+      const int64_t o = s.n_big + s.n_mid + q;
+      k.seg = s.order[o];
+      const int2 sp = *reinterpret_cast<const int2 *>(s.spans + 2 * o);
+      k.eb = sp.x;
+      k.ee = sp.y;
     }
   }
   return k;
@@ -852,12 +856,12 @@ bool shape_supported(gt_dtype dt, int heads, int head_dim) {
   return dispatch(dt, heads, head_dim, NopF{});
 }
 
-static Sched sched_of(const gt_sched &s, const int32_t *ptr) {
+static Sched sched_of(const gt_sched &s) {
   Sched r;
-  r.ptr = ptr;
   r.order = s.order;
   r.items = s.items;
   r.merges = s.merges;
+  r.spans = s.spans;
   r.n_big = s.n_big;
   r.n_mid = s.n_mid;
   r.n_small = s.n_small;
@@ -871,7 +875,7 @@ gt_status launch_fwd(const gt_graph *g, int heads, int head_dim, gt_dtype dt, fl
                      const void *Q, const void *K, const void *V, const float *bias, void *Y,
                      float *lse, float *part, hipStream_t st) {
   FwdArgs a;
-  a.s = sched_of(g->rows, g->indptr);
+  a.s = sched_of(g->rows);
   a.idx = g->indices;
   a.Q = Q;
   a.K = K;
@@ -893,8 +897,8 @@ gt_status launch_bwd(const gt_graph *g, int heads, int head_dim, gt_dtype dt, fl
                      void *dV, float *dbias, float *rowstat, float *part_rows, float *part_cols,
                      hipStream_t st) {
   BwdArgs a;
-  a.rows = sched_of(g->rows, g->indptr);
-  a.cols = sched_of(g->cols, g->indptr_t);
+  a.rows = sched_of(g->rows);
+  a.cols = sched_of(g->cols);
   a.idx = g->indices;
   a.idx_t = g->indices_t;
   a.perm = g->perm;

@@ -35,8 +35,8 @@ constexpr int64_t cols_slot_floats(int64_t D, int64_t) { return 2 * D; }
 
 struct MetaLayout {
   size_t indptr_t, indices_t, perm;
-  size_t row_order, row_items, row_merges;
-  size_t col_order, col_items, col_merges;
+  size_t row_order, row_items, row_merges, row_spans;
+  size_t col_order, col_items, col_merges, col_spans;
   size_t kA, vA, kB, vB, hist, bsum, misc;
   size_t total;
 };
@@ -57,9 +57,11 @@ inline bool meta_layout(int64_t R, int64_t M, int64_t E, int32_t chunk, MetaLayo
   L->row_order = take(R);
   L->row_items = take(4 * capR);
   L->row_merges = take(3 * capR);
+  L->row_spans = take(2 * R);
   L->col_order = take(M);
   L->col_items = take(4 * capM);
   L->col_merges = take(3 * capM);
+  L->col_spans = take(2 * M);
   const int64_t nmax = std::max<int64_t>({E, R, M, 1});
   const int64_t nblk = (nmax + SORT_TILE_ITEMS - 1) / SORT_TILE_ITEMS;
   const int64_t scan_len = std::max<int64_t>({256 * nblk, M + 1, R + 1});

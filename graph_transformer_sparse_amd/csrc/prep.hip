@@ -424,6 +424,14 @@ __global__ __launch_bounds__(WI_THREADS) void k_write_items(
   }
 }
 
+// spans[k] = (ptr[order[k]], ptr[order[k] + 1])
+__global__ void k_spans(const int32_t *ptr, const int32_t *order, int64_t n, int32_t *spans) {
+  const int64_t k = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (k >= n) return;
+  const int32_t sg = order[k];
+  *reinterpret_cast<int2 *>(spans + 2 * k) = make_int2(ptr[sg], ptr[sg + 1]);
+}
+
 static gt_status build_schedule(const int32_t *ptr, int64_t n, int32_t t_small, int32_t t_mid,
                                 int32_t chunk, const SortBufs &b, Misc *misc_d, gt_sched *out,
                                 hipStream_t s) {
@@ -444,8 +452,11 @@ static gt_status build_schedule(const int32_t *ptr, int64_t n, int32_t t_small, 
   uint32_t *ks, *vs;
   gt_status st = radix_sort(b.kA, nullptr, n, bits_for(m.max_degree), b, s, &ks, &vs);
   if (st != GT_OK) return st;
-  if (n > 0)
+  if (n > 0) {
     GT_HIP(hipMemcpyAsync(out->order, vs, sizeof(int32_t) * (size_t)n, hipMemcpyDeviceToDevice, s));
+    k_spans<<<dim3((unsigned)cdiv(n, TB)), dim3(TB), 0, s>>>(ptr, out->order, n, out->spans);
+    GT_CHECK_LAUNCH();
+  }
   const int64_t nb = m.n_big;
   uint32_t n_items = 0, n_merges = 0;
   if (nb > 0) {
@@ -548,9 +559,11 @@ extern "C" gt_status gt_graph_prepare(const int32_t *indptr, const int32_t *indi
   g.rows.order = (int32_t *)at(L.row_order);
   g.rows.items = (int32_t *)at(L.row_items);
   g.rows.merges = (int32_t *)at(L.row_merges);
+  g.rows.spans = (int32_t *)at(L.row_spans);
   g.cols.order = (int32_t *)at(L.col_order);
   g.cols.items = (int32_t *)at(L.col_items);
   g.cols.merges = (int32_t *)at(L.col_merges);
+  g.cols.spans = (int32_t *)at(L.col_spans);
   g.t_small = t_small;
   g.t_mid = t_mid;
   g.chunk = chunk;

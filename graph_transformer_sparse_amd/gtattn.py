@@ -33,7 +33,7 @@ _i64, _i32, _P, _f32, _sz = C.c_int64, C.c_int32, C.c_void_p, C.c_float, C.c_siz
 
 
 class GtSched(C.Structure):
-    _fields_ = [("order", _P), ("items", _P), ("merges", _P),
+    _fields_ = [("order", _P), ("items", _P), ("merges", _P), ("spans", _P),
                 ("n_seg", _i64), ("n_big", _i64), ("n_mid", _i64), ("n_small", _i64),
                 ("n_items", _i64), ("n_merges", _i64), ("max_degree", _i64)]
 
@@ -121,15 +121,20 @@ def _dt(dtype) -> int:
     raise TypeError(f"unsupported dtype {dtype}")
 
 
-def _need(cond: bool, where: str, msg: str):
+def _need(cond: bool, where: str, msg):
+    """Raise ValueError(where: msg) unless cond; msg may be a callable, so
+    that the text is only built on failure (these checks run on every call)."""
     if not cond:
-        raise ValueError(f"{where}: {msg}")
+        raise ValueError(f"{where}: {msg() if callable(msg) else msg}")
 
 
 def _tensor(where: str, name: str, t, shape, dtype, device):
     """Check that t is a contiguous tensor of this shape, dtype and device.
     The C ABI gets only pointers: a wrongly sized array would be read or
     written out of bounds on the GPU, so sizes are checked here."""
+    if (isinstance(t, torch.Tensor) and t.shape == shape and t.dtype == dtype
+            and t.device == device and t.is_contiguous()):
+        return
     _need(isinstance(t, torch.Tensor), where, f"{name} must be a tensor")
     _need(tuple(t.shape) == tuple(shape), where,
           f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
@@ -145,7 +150,7 @@ def _attn_shapes(where: str, g: "Graph", Q, K, V, bias):
           "head_dim] tensor")
     R, H, dh = Q.shape
     dt, dev = Q.dtype, Q.device
-    _need(dt in (torch.float32, torch.bfloat16), where, f"unsupported dtype {dt}")
+    _need(dt in (torch.float32, torch.bfloat16), where, lambda: f"unsupported dtype {dt}")
     _tensor(where, "Q", Q, (g.n_rows, H, dh), dt, dev)
     _tensor(where, "K", K, (g.n_cols, H, dh), dt, dev)
     _tensor(where, "V", V, (g.n_cols, H, dh), dt, dev)
@@ -155,8 +160,9 @@ def _attn_shapes(where: str, g: "Graph", Q, K, V, bias):
 
 
 def _on_gpu(where: str, g: "Graph", dev):
-    _need(dev.type == "cuda", where, f"tensors must be on a GPU, not {dev}")
-    _need(g.meta.device == dev, where, f"the graph is on {g.meta.device}, the tensors on {dev}")
+    _need(dev.type == "cuda", where, lambda: f"tensors must be on a GPU, not {dev}")
+    _need(g.meta.device == dev, where,
+          lambda: f"the graph is on {g.meta.device}, the tensors on {dev}")
 
 
 def gt_default_thresholds():
@@ -214,6 +220,7 @@ class Graph:
                     counts=(s.n_big, s.n_mid, s.n_small),
                     items=self._view(s.items, 4 * s.n_items).view(-1, 4),
                     merges=self._view(s.merges, 3 * s.n_merges).view(-1, 3),
+                    spans=self._view(s.spans, 2 * s.n_seg).view(-1, 2),
                     max_degree=s.max_degree)
 
 
@@ -407,12 +414,12 @@ def _proj_lib():
 def _nd(where: str, X, *others):
     """(n, d) of X [n, d]; `others` are (name, tensor, shape) to check against it."""
     _need(isinstance(X, torch.Tensor) and X.dim() == 2, where, "X must be a [n, d] tensor")
-    _need(X.dtype in (torch.float32, torch.bfloat16), where, f"unsupported dtype {X.dtype}")
+    _need(X.dtype in (torch.float32, torch.bfloat16), where, lambda: f"unsupported dtype {X.dtype}")
     _need(X.is_contiguous(), where, "X must be contiguous")
     n, d = X.shape
     for name, t, shape in others:
         _tensor(where, name, t, shape(n, d), X.dtype, X.device)
-    _need(X.device.type == "cuda", where, f"tensors must be on a GPU, X is on {X.device}")
+    _need(X.device.type == "cuda", where, lambda: f"tensors must be on a GPU, X is on {X.device}")
     return n, d
 
 
@@ -513,7 +520,7 @@ def _heads_geometry(t: torch.Tensor):
     """(rows, heads, head_bytes) of a contiguous [rows, heads, ...] tensor."""
     _need(isinstance(t, torch.Tensor) and t.dim() >= 2 and t.is_contiguous(), "head repack",
           "expects a contiguous [rows, heads, ...] tensor")
-    _need(t.device.type == "cuda", "head repack", f"tensors must be on a GPU, not {t.device}")
+    _need(t.device.type == "cuda", "head repack", lambda: f"tensors must be on a GPU, not {t.device}")
     rows, heads = t.shape[0], t.shape[1]
     per_head = t[0, 0].numel() if rows > 0 else math.prod(t.shape[2:])
     return rows, heads, int(per_head) * t.element_size()
@@ -537,7 +544,7 @@ def gt_head_merge(p: torch.Tensor, out=None) -> torch.Tensor:
     """The inverse of gt_head_split: [parts, rows, hp, ...] -> [rows, parts*hp, ...]."""
     _need(isinstance(p, torch.Tensor) and p.dim() >= 3 and p.is_contiguous(), "gt_head_merge",
           "expects a contiguous [parts, rows, heads/parts, ...] tensor")
-    _need(p.device.type == "cuda", "gt_head_merge", f"tensors must be on a GPU, not {p.device}")
+    _need(p.device.type == "cuda", "gt_head_merge", lambda: f"tensors must be on a GPU, not {p.device}")
     parts, rows, hp = p.shape[0], p.shape[1], p.shape[2]
     heads = parts * hp
     hb = math.prod(p.shape[3:]) * p.element_size()

@@ -247,7 +247,11 @@ def graph_for(cfg: Config):
         rows, cols = gnp_directed(R, 8.0, rng)
         return csr_from_pairs(rows, cols, R, M)
     if cfg.name == "mid":
-        rows, cols = rmat_pairs(17, 14 * R, rng)
+        # 2^17 nodes as configured; other powers of two give the same recipe
+        # at another node count
+        levels = int(R).bit_length() - 1
+        assert R == M == 1 << levels, "the R-MAT recipe needs a power-of-two node count"
+        rows, cols = rmat_pairs(levels, 14 * R, rng)
         return csr_from_pairs(rows, cols, R, M)
     if cfg.name == "large":
         u = 1.0 - rng.random(R)
@@ -344,10 +348,14 @@ _GRAPHS = {}   # the named graphs generated in this process
 def named_graph(cfg: Config):
     """graph_for(cfg), generated once per process (and read from / written
     to the directory GT_INPUT_CACHE names, if set)."""
-    if cfg.name in _GRAPHS:
-        return _GRAPHS[cfg.name]
+    # the graph depends on the recipe (name) and the node counts only
+    named = CONFIGS.get(cfg.name)
+    same = named is not None and (named.n_rows, named.n_cols) == (cfg.n_rows, cfg.n_cols)
+    key = cfg.name if same else f"{cfg.name}_{cfg.n_rows}x{cfg.n_cols}"
+    if key in _GRAPHS:
+        return _GRAPHS[key]
     cache = _cache_dir()
-    path = os.path.join(cache, f"graph_{cfg.name}.npz") if cache else None
+    path = os.path.join(cache, f"graph_{key}.npz") if cache else None
     if path and os.path.exists(path):
         with np.load(path) as z:
             graph = (z["indptr"], z["indices"])
@@ -358,7 +366,7 @@ def named_graph(cfg: Config):
             tmp = path + ".tmp.npz"
             np.savez(tmp, indptr=graph[0], indices=graph[1])
             os.replace(tmp, path)
-    _GRAPHS[cfg.name] = graph
+    _GRAPHS[key] = graph
     return graph
 
 

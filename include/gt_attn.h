@@ -94,7 +94,10 @@ typedef enum { GT_F32 = 0, GT_BF16 = 1 } gt_dtype;
  *              (s, ptr[s] + floor(c d / nch), ptr[s] + floor((c+1) d / nch),
  *              slot) where slot is the item's own index if nch > 1, else -1;
  *   merges   = [n_merges][3] int32: (s, first item, nch) for every big
- *              segment with nch > 1.
+ *              segment with nch > 1;
+ *   spans    = [n_seg][2] int32: (ptr[order[k]], ptr[order[k] + 1]), the
+ *              extent of the k-th segment of `order` (so a kernel finds a
+ *              segment's nonzeros without a second, dependent load).
  * Big pieces and mid segments are each processed by one 64-lane wavefront;
  * small segments by a group of lanes inside a wavefront.  Split segments
  * are reduced afterwards in piece order, so results are deterministic. */
@@ -102,6 +105,7 @@ typedef struct gt_sched {
   int32_t *order;   /* [n_seg] */
   int32_t *items;   /* [cap][4] */
   int32_t *merges;  /* [cap][3] */
+  int32_t *spans;   /* [n_seg][2] */
   int64_t n_seg, n_big, n_mid, n_small, n_items, n_merges, max_degree;
 } gt_sched;
 

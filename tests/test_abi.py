@@ -50,7 +50,7 @@ def _fake_graph(R=100, M=80, E=500, n_items=3):
     fake = 0x10000000
     g.indptr, g.indices, g.indptr_t, g.indices_t, g.perm = fake, fake, fake, fake, fake
     for s in (g.rows, g.cols):
-        s.order, s.items, s.merges = fake, fake, fake
+        s.order, s.items, s.merges, s.spans = fake, fake, fake, fake
         s.n_items = n_items
     return g
 

@@ -157,3 +157,6 @@ def test_prep_full_configs(name):
         assert tuple(got["counts"]) == tuple(int(c) for c in want["counts"]), which
         assert np.array_equal(got["items"].cpu().numpy(), want["items"]), which
         assert np.array_equal(got["merges"].cpu().numpy(), want["merges"]), which
+        o = np.asarray(want["order"], np.int64)
+        assert np.array_equal(got["spans"].cpu().numpy(),
+                              np.stack([ptr[o], ptr[o + 1]], axis=1).reshape(-1, 2)), which

@@ -52,6 +52,10 @@ def _check_sched(got, ptr, ts, tm, ch):
     assert tuple(got["counts"]) == tuple(int(c) for c in want["counts"])
     np.testing.assert_array_equal(got["items"].cpu().numpy(), want["items"])
     np.testing.assert_array_equal(got["merges"].cpu().numpy(), want["merges"])
+    # extents of the ordered segments, from the oracle's order and the CSR pointer
+    o = np.asarray(want["order"], np.int64)
+    np.testing.assert_array_equal(got["spans"].cpu().numpy(),
+                                  np.stack([ptr[o], ptr[o + 1]], axis=1).reshape(-1, 2))
     assert got["max_degree"] == (int(np.max(np.diff(ptr))) if ptr.size > 1 else 0)
 
 
