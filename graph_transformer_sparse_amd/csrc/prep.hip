@@ -526,6 +526,14 @@ extern "C" void gt_default_thresholds(int32_t *t_small, int32_t *t_mid, int32_t 
   if (chunk) *chunk = DEFAULT_CHUNK;
 }
 
+extern "C" void gt_graph_thresholds(int64_t nnz, int32_t *t_small, int32_t *t_mid,
+                                    int32_t *chunk) {
+  const int32_t c = chunk_for(nnz);
+  if (t_small) *t_small = DEFAULT_T_SMALL;
+  if (t_mid) *t_mid = c;
+  if (chunk) *chunk = c;
+}
+
 extern "C" gt_status gt_graph_prepare(const int32_t *indptr, const int32_t *indices,
                                       int64_t n_rows, int64_t n_cols, int64_t nnz,
                                       int32_t t_small, int32_t t_mid, int32_t chunk, void *meta,

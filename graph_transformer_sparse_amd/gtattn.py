@@ -6,7 +6,7 @@ step of the computation runs in the library's kernels.  If the library has
 not been built, every entry point raises; there is no fallback.
 
 Names follow the C ABI: gt_graph_prepare, gt_attn_fwd, gt_attn_bwd,
-gt_attn_work_bytes, gt_csr_validate, gt_default_thresholds, plus the
+gt_attn_work_bytes, gt_csr_validate, gt_default_thresholds, gt_graph_thresholds, plus the
 autograd wrapper GTAttnFn / sparse_graph_attention.
 """
 from __future__ import annotations
@@ -78,6 +78,7 @@ def lib():
         "gt_graph_meta_bytes": (_sz, [_i64, _i64, _i64, _i32]),
         "gt_graph_prepare": (_i32, [_P, _P, _i64, _i64, _i64, _i32, _i32, _i32, _P, _sz, G, _P]),
         "gt_default_thresholds": (None, [C.POINTER(_i32)] * 3),
+        "gt_graph_thresholds": (None, [_i64] + [C.POINTER(_i32)] * 3),
         "gt_csr_validate": (_i32, [_P, _P, _i64, _i64, _i64, _P, _sz, C.POINTER(_i32), _P]),
         "gt_attn_work_bytes": (_sz, [G, _i32, _i32]),
         "gt_attn_fwd": (_i32, [G, _i32, _i32, _i32, _f32, _P, _P, _P, _P, _P, _P, _P, _sz, _P]),
@@ -171,6 +172,13 @@ def gt_default_thresholds():
     return a.value, b.value, c.value
 
 
+def gt_graph_thresholds(nnz: int):
+    """(t_small, t_mid, chunk) tuned for a graph of nnz nonzeros."""
+    a, b, c = _i32(), _i32(), _i32()
+    lib().gt_graph_thresholds(int(nnz), C.byref(a), C.byref(b), C.byref(c))
+    return a.value, b.value, c.value
+
+
 class Graph:
     """A CSR adjacency prepared for attention (transpose and schedules).
 
@@ -244,7 +252,7 @@ def gt_graph_prepare(indptr: torch.Tensor, indices: torch.Tensor, n_cols: int,
         code = gt_csr_validate(indptr, indices, n_cols)
         if code != 0:
             raise GTError(8, "gt_graph_prepare", f"malformed CSR (gt_csr_validate code {code})")
-    d_small, d_mid, d_chunk = gt_default_thresholds()
+    d_small, d_mid, d_chunk = gt_graph_thresholds(indices.numel())
     t_small = d_small if t_small is None else t_small
     t_mid = d_mid if t_mid is None else t_mid
     chunk = d_chunk if chunk is None else chunk

@@ -134,7 +134,7 @@ size_t gt_graph_meta_bytes(int64_t n_rows, int64_t n_cols, int64_t nnz, int32_t 
  *   of a column are ordered by ascending source row (a stable transpose);
  *   indices_t[t] = source row, perm[t] = CSR edge id (the adjacency's
  *   transpose is what the backward's A^T products of Section 2.2 run on).
- *   Thresholds: 0 <= t_small <= t_mid, chunk >= 1 (gt_default_thresholds).
+ *   Thresholds: 0 <= t_small <= t_mid, chunk >= 1 (gt_graph_thresholds).
  * Synchronises `stream` (the schedule sizes are read back to fill *out).
  * Errors: GT_E_NULL, GT_E_ARG, GT_E_WORKSPACE (meta_bytes too small),
  * GT_E_HIP. */
@@ -143,8 +143,14 @@ gt_status gt_graph_prepare(const int32_t *indptr, const int32_t *indices, int64_
                            int32_t chunk, void *meta, size_t meta_bytes, gt_graph *out,
                            void *stream);
 
-/* The thresholds the kernels are tuned for: t_small, t_mid, chunk. */
+/* The thresholds the kernels are tuned for: t_small, t_mid, chunk (those of
+ * graphs below 8M nonzeros). */
 void gt_default_thresholds(int32_t *t_small, int32_t *t_mid, int32_t *chunk);
+
+/* The tuned thresholds for a graph of nnz nonzeros: as gt_default_thresholds,
+ * except that pieces (chunk = t_mid) grow to 2048 nonzeros from 8M nonzeros
+ * on, where a pass is long enough for a wavefront to walk them. */
+void gt_graph_thresholds(int64_t nnz, int32_t *t_small, int32_t *t_mid, int32_t *chunk);
 
 /* Debug check of CSR content (the oracle's codes): 0 valid; 1 indptr[0] != 0
  * or indptr[n_rows] != nnz; 2 indptr decreasing; 3 a column outside

@@ -149,7 +149,8 @@ def test_prep_full_configs(name):
     assert np.array_equal(g.indptr_t.cpu().numpy(), pt)
     assert np.array_equal(g.indices_t.cpu().numpy(), it)
     assert np.array_equal(g.perm.cpu().numpy(), pm)
-    ts, tm, ch = T.gt_default_thresholds()
+    ts, tm, ch = g.st.t_small, g.st.t_mid, g.st.chunk   # what prepare chose for this size
+    assert (ts, tm, ch) == T.gt_graph_thresholds(ix.size)
     print(f"prep {name}: oracle schedules", flush=True)
     for which, ptr in (("rows", ip), ("cols", pt)):
         got, want = g.schedule(which), O.schedule(ptr, ts, tm, ch)

@@ -83,7 +83,8 @@ def test_mid_config_prep():
     np.testing.assert_array_equal(g.indptr_t.cpu().numpy(), pt)
     np.testing.assert_array_equal(g.indices_t.cpu().numpy(), it)
     np.testing.assert_array_equal(g.perm.cpu().numpy(), pm)
-    ts, tm, ch = T.gt_default_thresholds()
+    ts, tm, ch = g.st.t_small, g.st.t_mid, g.st.chunk   # what prepare chose for this size
+    assert (ts, tm, ch) == T.gt_graph_thresholds(ix.size)
     _check_sched(g.schedule("rows"), ip, ts, tm, ch)
     _check_sched(g.schedule("cols"), pt, ts, tm, ch)
 
