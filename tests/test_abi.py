@@ -171,3 +171,22 @@ def test_heads_argument_checks(L):
     assert L.gt_head_merge(10, 8, 64, 2, None, FAKE, None) == 1
     assert L.gt_head_split(10, 8, 64, 2, FAKE, C.c_void_p(0x20000002), None) == 5  # alignment
     assert L.gt_head_split(0, 8, 64, 2, None, None, None) == 0      # nothing to move
+
+
+def test_library_imports_no_device_allocator(L):
+    """The library allocates no device or pinned memory: every buffer is the
+    caller's (meta, work, inputs and outputs).  Checked on the shared
+    object's imported symbols, so no code path can call an allocator."""
+    import shutil
+    import subprocess
+    nm = shutil.which("nm")
+    if nm is None:
+        pytest.skip("nm not available")
+    out = subprocess.run([nm, "-D", "--undefined-only", B.LIB], capture_output=True, text=True,
+                         check=True).stdout
+    names = [ln.split()[-1].split("@")[0] for ln in out.splitlines() if ln.strip()]
+    assert "hipLaunchKernel" in names          # the listing is the real one
+    alloc = [n for n in names if n.startswith(("hipMalloc", "hipFree", "hipHostMalloc",
+                                               "hipHostAlloc", "hipExtMalloc", "hipMallocManaged",
+                                               "hipMemPool"))]
+    assert alloc == [], alloc

@@ -118,6 +118,38 @@ def test_bitwise_determinism():
             assert torch.equal(x, y) and torch.equal(x, z)
 
 
+def test_one_graph_two_concurrent_streams():
+    """One prepared graph, two streams running forward and backward at the
+    same time on different inputs (each call with its own work buffer): the
+    library keeps no state between calls, so each stream's results are
+    bitwise those of a lone run."""
+    ip, ix = I.random_graph(31, 400, 400, _degrees(np.random.default_rng(31), 400, 400))
+    probs = [I.small_problem(31 + k, ip, ix, 400, 4, 32, "bf16", True) for k in range(2)]
+    devs = [device_problem(P) for P in probs]
+    g = T.gt_graph_prepare(devs[0]["indptr"], devs[0]["indices"], 400, 2, 8, 8)
+
+    def step(d, P):
+        Y, lse = T.gt_attn_fwd(g, d["Q"], d["K"], d["V"], d["bias"], P.scale)
+        return (Y, lse) + T.gt_attn_bwd(g, d["Q"], d["K"], d["V"], lse, d["dY"], d["bias"], P.scale)
+
+    alone = [step(d, P) for d, P in zip(devs, probs)]
+    torch.cuda.synchronize()
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    for st in streams:
+        st.wait_stream(torch.cuda.current_stream())
+    outs = [[], []]
+    for _ in range(4):                       # interleaved, no synchronisation in between
+        for k in range(2):
+            with torch.cuda.stream(streams[k]):
+                outs[k].append(step(devs[k], probs[k]))
+    torch.cuda.synchronize()
+    for k in range(2):
+        for got in outs[k]:
+            for x, y in zip(got, alone[k]):
+                assert torch.equal(x, y)
+    assert not torch.equal(alone[0][0], alone[1][0])    # the two inputs differ
+
+
 @pytest.mark.parametrize("limit", ["1", "3"])
 def test_grid_in_several_launches(limit, monkeypatch):
     """Grids larger than one launch allows go out in several launches, each
