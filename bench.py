@@ -184,6 +184,11 @@ def cpu_baseline(P, budget_s: float, gpu_rows=None):
         O.set_threads(cores)
     out["single_thread"] = {"value": e1 * runs1 / total1 / 1e9, "unit": "GEdges/s",
                             "sample": f"rows 0..{k1 - 1}, {runs1} run(s) in {total1:.1f} s"}
+    # the oracle's own CSR transpose of the whole graph (serial counting
+    # sort), the step the GPU's prepare does once per graph
+    t = time.perf_counter()
+    O.transpose(P.indptr, P.indices, cfg.n_cols)
+    out["transpose_s"] = time.perf_counter() - t
     if gpu_rows is not None:
         out["parity"] = parity_on_block(P, k, e, run, gpu_rows)
     return out
