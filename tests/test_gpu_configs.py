@@ -11,6 +11,8 @@ benchmark times (default thresholds):
 
 Set GT_INPUT_CACHE to a directory to reuse generated graphs across runs.
 """
+import dataclasses
+
 import numpy as np
 import pytest
 import torch
@@ -82,9 +84,16 @@ def _invariants(P, o, rtol):
                                      f"{a[i]!r}, |D| {Dh[i, h]!r}, degree {P.indptr[i + 1] - P.indptr[i]}")
 
 
-def test_mid_full():
-    P = I.make_problem(I.CONFIGS["mid"])
-    print("mid: gpu", flush=True)
+@pytest.mark.parametrize("hidden", [128, 64, 256])
+def test_mid_full(hidden):
+    """The Mid workload (hidden 128 over 8 heads) and the same graph at the
+    pages' other hidden sizes, 64 and 256 (Figure 7: head_dim 8 and 32),
+    every output against the oracle."""
+    cfg = I.CONFIGS["mid"]
+    if hidden != cfg.heads * cfg.head_dim:
+        cfg = dataclasses.replace(cfg, head_dim=hidden // cfg.heads)
+    P = I.make_problem(cfg)
+    print(f"mid hidden {hidden}: gpu", flush=True)
     o = _run(P)
     assert o["n_split_rows"] > 0 and o["n_split_cols"] > 0
     print("mid: oracle", flush=True)
