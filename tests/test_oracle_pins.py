@@ -134,6 +134,7 @@ CASES = [
     (2, 48, 64, 2, 4, True),
     (3, 64, 30, 4, 16, True),
     (4, 33, 33, 2, 32, False),
+    (5, 20, 24, 2, 128, True),
 ]
 
 
