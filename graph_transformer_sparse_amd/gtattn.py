@@ -107,7 +107,8 @@ def _check(status: int, where: str):
 
 
 def _ptr(t):
-    return None if t is None else C.c_void_p(t.data_ptr())
+    # a plain int: ctypes converts it for c_void_p parameters
+    return None if t is None else t.data_ptr()
 
 
 def _stream(device=None):
@@ -190,18 +191,10 @@ class Graph:
         self.meta = meta
         self.indptr = indptr
         self.indices = indices
-
-    @property
-    def n_rows(self):
-        return self.st.n_rows
-
-    @property
-    def n_cols(self):
-        return self.st.n_cols
-
-    @property
-    def nnz(self):
-        return self.st.nnz
+        # plain copies of the sizes (read on every call) and the work sizes
+        # asked for so far, per (heads, head_dim)
+        self.n_rows, self.n_cols, self.nnz = int(st.n_rows), int(st.n_cols), int(st.nnz)
+        self._work_bytes = {}
 
     def _view(self, ptr: int, n: int) -> torch.Tensor:
         base = self.meta.data_ptr()
@@ -289,7 +282,11 @@ def gt_csr_validate(indptr: torch.Tensor, indices: torch.Tensor, n_cols: int) ->
 
 
 def gt_attn_work_bytes(g: Graph, heads: int, head_dim: int) -> int:
-    return int(lib().gt_attn_work_bytes(C.byref(g.st), heads, head_dim))
+    key = (heads, head_dim)
+    nb = g._work_bytes.get(key)
+    if nb is None:
+        nb = g._work_bytes[key] = int(lib().gt_attn_work_bytes(C.byref(g.st), heads, head_dim))
+    return nb
 
 
 def _work(g, heads, head_dim, device, work):
