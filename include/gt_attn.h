@@ -214,6 +214,7 @@ gt_status gt_prof_query(const char *kernel, double *total_ms, int64_t *launches)
 const char *gt_status_str(gt_status s);
 /* Detail of the last failed call on this thread ("" if none). */
 const char *gt_last_error(void);
+/* Version of the ABI: 101 (the schedule carries the segment extents `spans`). */
 int32_t gt_version(void);
 
 #ifdef __cplusplus
