@@ -432,58 +432,82 @@ __global__ void k_spans(const int32_t *ptr, const int32_t *order, int64_t n, int
   *reinterpret_cast<int2 *>(spans + 2 * k) = make_int2(ptr[sg], ptr[sg + 1]);
 }
 
-static gt_status build_schedule(const int32_t *ptr, int64_t n, int32_t t_small, int32_t t_mid,
-                                int32_t chunk, const SortBufs &b, Misc *misc_d, gt_sched *out,
-                                hipStream_t s) {
-  GT_HIP(hipMemsetAsync(misc_d, 0, sizeof(Misc), s));
+// The two schedules (rows of A and of A^T) are built side by side, so that
+// the host reads their sizes back twice in all (after the degree statistics
+// and after the piece lists) instead of twice per schedule.
+struct SchedJob {
+  const int32_t *ptr;   // segment pointer (indptr or indptr_t)
+  int64_t n;            // segments
+  Misc *misc_d;         // this schedule's device counters
+  gt_sched *out;
+  Misc m;               // host copy of the counters
+};
+
+static gt_status build_schedules(SchedJob (&jobs)[2], int32_t t_small, int32_t t_mid,
+                                 int32_t chunk, const SortBufs &b, hipStream_t s) {
   const int TB = 256;
-  if (n > 0) {
-    const int64_t nblk = std::min<int64_t>(cdiv(n, DS_THREADS), DS_MAX_BLOCKS);
-    k_degree_stats<<<dim3((unsigned)nblk), dim3(DS_THREADS), 0, s>>>(ptr, n, t_small, t_mid, misc_d);
-    GT_CHECK_LAUNCH();
+  // phase 1: degree statistics of both
+  for (SchedJob &j : jobs) {
+    GT_HIP(hipMemsetAsync(j.misc_d, 0, sizeof(Misc), s));
+    if (j.n > 0) {
+      const int64_t nblk = std::min<int64_t>(cdiv(j.n, DS_THREADS), DS_MAX_BLOCKS);
+      k_degree_stats<<<dim3((unsigned)nblk), dim3(DS_THREADS), 0, s>>>(j.ptr, j.n, t_small, t_mid,
+                                                                       j.misc_d);
+      GT_CHECK_LAUNCH();
+    }
   }
-  Misc m;
-  GT_HIP(hipMemcpyAsync(&m, misc_d, sizeof(Misc), hipMemcpyDeviceToHost, s));
+  for (SchedJob &j : jobs)
+    GT_HIP(hipMemcpyAsync(&j.m, j.misc_d, sizeof(Misc), hipMemcpyDeviceToHost, s));
   GT_HIP(hipStreamSynchronize(s));
-  if (n > 0) {
-    k_degree_keys<<<dim3((unsigned)cdiv(n, TB)), dim3(TB), 0, s>>>(ptr, n, m.max_degree, b.kA);
-    GT_CHECK_LAUNCH();
-  }
-  uint32_t *ks, *vs;
-  gt_status st = radix_sort(b.kA, nullptr, n, bits_for(m.max_degree), b, s, &ks, &vs);
-  if (st != GT_OK) return st;
-  if (n > 0) {
-    GT_HIP(hipMemcpyAsync(out->order, vs, sizeof(int32_t) * (size_t)n, hipMemcpyDeviceToDevice, s));
-    k_spans<<<dim3((unsigned)cdiv(n, TB)), dim3(TB), 0, s>>>(ptr, out->order, n, out->spans);
-    GT_CHECK_LAUNCH();
-  }
-  const int64_t nb = m.n_big;
-  uint32_t n_items = 0, n_merges = 0;
-  if (nb > 0) {
-    // piece counts and split flags of the big segments, then their offsets
-    uint32_t *nch = b.kA, *split = b.kB, *ioff = b.vA, *moff = b.vB;
-    k_piece_counts<<<dim3((unsigned)cdiv(nb, TB)), dim3(TB), 0, s>>>(ptr, out->order, nb, chunk,
-                                                                      nch, split);
-    GT_CHECK_LAUNCH();
-    st = excl_scan(nch, ioff, nb, b.bsum, &misc_d->n_items, s);
+  // phase 2: degree order, extents and piece lists of each (the sort
+  // scratch is reused in stream order)
+  for (SchedJob &j : jobs) {
+    gt_sched *out = j.out;
+    const int64_t n = j.n;
+    if (n > 0) {
+      k_degree_keys<<<dim3((unsigned)cdiv(n, TB)), dim3(TB), 0, s>>>(j.ptr, n, j.m.max_degree,
+                                                                     b.kA);
+      GT_CHECK_LAUNCH();
+    }
+    uint32_t *ks, *vs;
+    gt_status st = radix_sort(b.kA, nullptr, n, bits_for(j.m.max_degree), b, s, &ks, &vs);
     if (st != GT_OK) return st;
-    st = excl_scan(split, moff, nb, b.bsum, &misc_d->n_merges, s);
-    if (st != GT_OK) return st;
-    k_write_items<<<dim3((unsigned)cdiv(nb, WI_THREADS / WAVE)), dim3(WI_THREADS), 0, s>>>(
-        ptr, out->order, nb, ioff, moff, chunk, out->items, out->merges);
-    GT_CHECK_LAUNCH();
-    GT_HIP(hipMemcpyAsync(&m, misc_d, sizeof(Misc), hipMemcpyDeviceToHost, s));
-    GT_HIP(hipStreamSynchronize(s));
-    n_items = m.n_items;
-    n_merges = m.n_merges;
+    if (n > 0) {
+      GT_HIP(hipMemcpyAsync(out->order, vs, sizeof(int32_t) * (size_t)n, hipMemcpyDeviceToDevice,
+                            s));
+      k_spans<<<dim3((unsigned)cdiv(n, TB)), dim3(TB), 0, s>>>(j.ptr, out->order, n, out->spans);
+      GT_CHECK_LAUNCH();
+    }
+    const int64_t nb = j.m.n_big;
+    if (nb > 0) {
+      // piece counts and split flags of the big segments, then their offsets
+      uint32_t *nch = b.kA, *split = b.kB, *ioff = b.vA, *moff = b.vB;
+      k_piece_counts<<<dim3((unsigned)cdiv(nb, TB)), dim3(TB), 0, s>>>(j.ptr, out->order, nb,
+                                                                        chunk, nch, split);
+      GT_CHECK_LAUNCH();
+      st = excl_scan(nch, ioff, nb, b.bsum, &j.misc_d->n_items, s);
+      if (st != GT_OK) return st;
+      st = excl_scan(split, moff, nb, b.bsum, &j.misc_d->n_merges, s);
+      if (st != GT_OK) return st;
+      k_write_items<<<dim3((unsigned)cdiv(nb, WI_THREADS / WAVE)), dim3(WI_THREADS), 0, s>>>(
+          j.ptr, out->order, nb, ioff, moff, chunk, out->items, out->merges);
+      GT_CHECK_LAUNCH();
+    }
   }
-  out->n_seg = n;
-  out->n_big = m.n_big;
-  out->n_mid = m.n_mid;
-  out->n_small = m.n_small;
-  out->n_items = n_items;
-  out->n_merges = n_merges;
-  out->max_degree = m.max_degree;
+  for (SchedJob &j : jobs)
+    if (j.m.n_big > 0)
+      GT_HIP(hipMemcpyAsync(&j.m, j.misc_d, sizeof(Misc), hipMemcpyDeviceToHost, s));
+  GT_HIP(hipStreamSynchronize(s));
+  for (SchedJob &j : jobs) {
+    gt_sched *out = j.out;
+    out->n_seg = j.n;
+    out->n_big = j.m.n_big;
+    out->n_mid = j.m.n_mid;
+    out->n_small = j.m.n_small;
+    out->n_items = j.m.n_big > 0 ? j.m.n_items : 0;
+    out->n_merges = j.m.n_big > 0 ? j.m.n_merges : 0;
+    out->max_degree = j.m.max_degree;
+  }
   return GT_OK;
 }
 
@@ -577,7 +601,8 @@ extern "C" gt_status gt_graph_prepare(const int32_t *indptr, const int32_t *indi
   g.chunk = chunk;
   SortBufs b{(uint32_t *)at(L.kA), (uint32_t *)at(L.vA), (uint32_t *)at(L.kB),
              (uint32_t *)at(L.vB), (uint32_t *)at(L.hist), (uint32_t *)at(L.bsum)};
-  Misc *misc = (Misc *)at(L.misc);
+  static_assert(2 * sizeof(Misc) <= 64 * sizeof(int32_t), "meta holds two Misc");
+  Misc *misc = (Misc *)at(L.misc);   // [0] rows of A, [1] rows of A^T
   const int TB = 256;
 
   // perm: edge ids stably sorted by column; indptr_t: where each column's
@@ -600,9 +625,8 @@ extern "C" gt_status gt_graph_prepare(const int32_t *indptr, const int32_t *indi
                                                                       g.indices_t);
     GT_CHECK_LAUNCH();
   }
-  st = build_schedule(indptr, n_rows, t_small, t_mid, chunk, b, misc, &g.rows, s);
-  if (st != GT_OK) return st;
-  st = build_schedule(g.indptr_t, n_cols, t_small, t_mid, chunk, b, misc, &g.cols, s);
+  SchedJob jobs[2] = {{indptr, n_rows, misc, &g.rows, {}}, {g.indptr_t, n_cols, misc + 1, &g.cols, {}}};
+  st = build_schedules(jobs, t_small, t_mid, chunk, b, s);
   if (st != GT_OK) return st;
   GT_HIP(hipStreamSynchronize(s));
   *out = g;
