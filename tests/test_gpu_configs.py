@@ -84,16 +84,18 @@ def _invariants(P, o, rtol):
                                      f"{a[i]!r}, |D| {Dh[i, h]!r}, degree {P.indptr[i + 1] - P.indptr[i]}")
 
 
-@pytest.mark.parametrize("hidden", [128, 64, 256])
-def test_mid_full(hidden):
-    """The Mid workload (hidden 128 over 8 heads) and the same graph at the
-    pages' other hidden sizes, 64 and 256 (Figure 7: head_dim 8 and 32),
-    every output against the oracle."""
+@pytest.mark.parametrize("hidden, nodes", [(128, 1 << 17), (64, 1 << 17), (256, 1 << 17),
+                                           (128, 1 << 16), (128, 1 << 18)])
+def test_mid_full(hidden, nodes):
+    """The Mid workload (hidden 128 over 8 heads, 2^17 nodes), the same graph
+    at the pages' other hidden sizes, 64 and 256 (Figure 7: head_dim 8 and
+    32), and the same recipe at 2^16 and 2^18 nodes (Figure 6's axis), every
+    output against the oracle."""
     cfg = I.CONFIGS["mid"]
-    if hidden != cfg.heads * cfg.head_dim:
-        cfg = dataclasses.replace(cfg, head_dim=hidden // cfg.heads)
+    if hidden != cfg.heads * cfg.head_dim or nodes != cfg.n_rows:
+        cfg = dataclasses.replace(cfg, head_dim=hidden // cfg.heads, n_rows=nodes, n_cols=nodes)
     P = I.make_problem(cfg)
-    print(f"mid hidden {hidden}: gpu", flush=True)
+    print(f"mid hidden {hidden} nodes {nodes}: gpu", flush=True)
     o = _run(P)
     assert o["n_split_rows"] > 0 and o["n_split_cols"] > 0
     print("mid: oracle", flush=True)
