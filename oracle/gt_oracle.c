@@ -29,7 +29,9 @@
  * divides by sqrt(d)); head h is channels [h*dh, (h+1)*dh) of a node row;
  * the optional bias is added unscaled to the score before the softmax (the
  * MegaGraph page, Section III-A1, mechanism 3); an empty row gives Y = 0,
- * lse = -inf, dQ = 0; an empty column gives dK = dV = 0.
+ * lse = -inf, dQ = 0; an empty column gives dK = dV = 0.  A bias of -inf
+ * masks its edge: the edge gets weight 0 (exactly as if it were not stored)
+ * and dbias 0, and a row whose every edge is masked is an empty row.
  *
  * Inputs Q, K, V, dY and bias are double arrays (float32 and bf16 data arrive
  * widened exactly); every product and sum is done in double.
@@ -207,10 +209,17 @@ static void row_pass(const prob_t *p, i64 i, double *U, double *dU, double *dS,
       U[k * H + h] = s;
       if (s > m) m = s;
     }
+    /* A score of -inf (an edge masked by a -inf bias) gets weight 0, the
+     * same as an edge that is not stored; a row whose every score is -inf
+     * has no support and is treated as an empty row (U = 0, lse = -inf). */
     double l = 0.0;
-    for (i64 k = 0; k < deg; ++k) l += exp(U[k * H + h] - m);
-    for (i64 k = 0; k < deg; ++k) U[k * H + h] = exp(U[k * H + h] - m) / l;
-    if (o->lse) o->lse[h] = deg ? m + log(l) : -INFINITY;
+    if (m > -INFINITY) {
+      for (i64 k = 0; k < deg; ++k) l += exp(U[k * H + h] - m);
+      for (i64 k = 0; k < deg; ++k) U[k * H + h] = exp(U[k * H + h] - m) / l;
+    } else {
+      for (i64 k = 0; k < deg; ++k) U[k * H + h] = 0.0;
+    }
+    if (o->lse) o->lse[h] = l > 0.0 ? m + log(l) : -INFINITY;
     for (int c = 0; c < dh; ++c) {
       double y = 0.0, ya = 0.0;
       for (i64 k = 0; k < deg; ++k) {
@@ -467,7 +476,8 @@ void or_cols(i64 R, i64 M, int H, int dh, double scale, const i32 *indptr, const
       }
       for (i64 t = cnt[k]; t < cnt[k + 1]; ++t) {
         i64 i = in_row[t], e = in_edge[t];
-        double u = exp(score(&p, i, e, h) - lse[i * H + h]);
+        /* weight 0 for every edge of a row without support (lse = -inf) */
+        double u = lse[i * H + h] > -INFINITY ? exp(score(&p, i, e, h) - lse[i * H + h]) : 0.0;
         double du = dot_head(dY + i * D + (i64)h * dh, V + j * D + (i64)h * dh, dh);
         double ds = u * (du - Dr[i * H + h]);
         double tm = u * (fabs(du) + fabs(Dr[i * H + h]));

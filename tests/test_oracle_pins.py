@@ -301,6 +301,52 @@ def test_empty_rows_and_columns():
         np.testing.assert_array_equal(dV[j], 0.0)
 
 
+def test_minus_inf_bias_masks_the_edge():
+    """A bias of -inf on an edge gives that edge weight 0: every output is
+    the one of the same graph with the edge removed (the softmax runs over
+    the row's remaining neighbours), and its dbias is 0.  A row whose every
+    edge is masked equals an empty row (Y = 0, lse = -inf, dQ = 0).  The
+    reference is the oracle's ordinary path on the reduced graph, pinned by
+    the tests above."""
+    R, M, H = 40, 30, 2
+    degs = np.random.default_rng(5).integers(1, 12, R)
+    P = _rand_problem(41, R, M, H, 8, degs, bias=True, self_loops=False)
+    rng = np.random.default_rng(6)
+    E = P.indices.size
+    mask = rng.random((E, H)) < 0.3
+    rows = np.repeat(np.arange(R), np.diff(P.indptr))
+    for i in (0, 7, 19):                         # rows masked entirely, in head 0
+        mask[P.indptr[i]:P.indptr[i + 1], 0] = True
+    for i in (3, 11):                            # ... and in every head
+        mask[P.indptr[i]:P.indptr[i + 1], :] = True
+    b = np.where(mask, -np.inf, P.bias)
+    Y, lse = O.fwd(P.indptr, P.indices, M, P.Q, P.K, P.V, b)
+    dQ, dK, dV, dB = O.bwd(P.indptr, P.indices, M, P.Q, P.K, P.V, P.dY, b)
+    for a in (Y, lse[np.isfinite(lse)], dQ, dK, dV, dB):
+        assert np.all(np.isfinite(a))
+    np.testing.assert_array_equal(dB[mask], 0.0)
+    for h in range(H):
+        keep = ~mask[:, h]
+        ip = np.zeros(R + 1, np.int64)
+        np.cumsum(np.bincount(rows[keep], minlength=R), out=ip[1:])
+        sl = lambda x: np.ascontiguousarray(x[:, h:h + 1])
+        Yr, lr = O.fwd(ip, P.indices[keep], M, sl(P.Q), sl(P.K), sl(P.V), sl(P.bias[keep]))
+        gr = O.bwd(ip, P.indices[keep], M, sl(P.Q), sl(P.K), sl(P.V), sl(P.dY),
+                   sl(P.bias[keep]))
+        _close(Y[:, h:h + 1], Yr)
+        np.testing.assert_array_equal(np.isneginf(lse[:, h]), np.isneginf(lr[:, 0]))
+        f = np.isfinite(lr[:, 0])
+        _close(lse[f, h], lr[f, 0])
+        _close(dQ[:, h:h + 1], gr[0])
+        _close(dK[:, h:h + 1], gr[1])
+        _close(dV[:, h:h + 1], gr[2])
+        _close(dB[keep, h], gr[3][:, 0])
+    for i in (0, 7, 19, 3, 11):
+        np.testing.assert_array_equal(Y[i, 0], 0.0)
+        assert np.isneginf(lse[i, 0])
+        np.testing.assert_array_equal(dQ[i, 0], 0.0)
+
+
 # ----------------------------------------------------------------------------
 # invariants and equivariance
 # ----------------------------------------------------------------------------
