@@ -7,21 +7,33 @@ columns).  The graph is prepared once, outside the timed region (its time is
 reported separately); inputs, outputs and workspaces are resident in HBM and
 allocated before timing.
 
+With no --config, all five workloads run one after another; the last, the
+hub workload (2.4M nodes, 62M edges, per-edge bias: the pages' ogbn-products
+scale), is the headline and the other four go into detail.configs.  For each
+workload the outputs of the timed run are checked against the fp64 oracle
+on the whole graph (every output element, the tests' tolerance), and for the
+headline the oracle is also timed on this host's cores on a bounded sample.
+
 Prints ONE JSON line (rank 0) with the throughput in GEdges/s (edges =
 stored nonzeros, self-loops included) and, for the dominant kernel, the
 achieved fraction of the HBM roofline from the byte model below, timed with
 HIP events inside the library on the stream the kernels run on (only the
 dominant kernel, picked in three profiled steps after the warm-up, carries
 events in the timed region; the other kernels' times in "detail" come from
-those three steps).  Beside it,
-the fp64 CPU oracle is timed on this host's cores on a bounded sample of the
-same workload.
+those three steps).  roofline.unique_frac divides the step's compulsory
+bytes (every array once) by the step time, and roofline.counter_frac the
+step's counter-measured bytes (a stored rocprofv3 record in profiles/, used
+only while the kernel sources hash the same).
 
 Byte model (algorithmic bytes: what each kernel must move between HBM and
-the ALUs; s = bytes per element, D = H*dh, b = 1 with a per-edge bias):
+the ALUs; s = bytes per element, D = H*dh, b = 1 with a per-edge bias, y = 1
+when the row pass reads Y, which it does with a bias):
   fwd       R (4 + 2Ds + 4H)                     + E (4 + 2Ds + 4Hb)
-  bwd_rows  R (4 + 3Ds + 12H)                    + E (4 + 2Ds + 4Hb)
-  bwd_cols  M (4 + 2Ds) + M_nz 2Ds               + E (4 + 2Ds + 8H + (4 + 8H)b)
+  bwd_rows  R (4 + (3 + y)Ds + 12H)              + E (4 + 2Ds + 8Hb)
+  bwd_cols  M (4 + 2Ds) + M_nz 2Ds               + E (4 + 2Ds + 8H + (4 + 4H)b)
+With a bias the row pass stages each edge's score gradient in dbias and a
+streaming pass (bwd_dbias, E 8H + R 8H bytes) finishes it; its bytes are
+reported with that kernel but are not part of the step's model above.
 """
 from __future__ import annotations
 
@@ -40,20 +52,34 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
-KERNELS = ["fwd", "fwd_merge", "bwd_rows", "bwd_rows_merge", "bwd_cols", "bwd_cols_merge"]
+KERNELS = ["fwd", "fwd_merge", "bwd_rows", "bwd_rows_merge", "bwd_cols", "bwd_cols_merge",
+           "bwd_dbias"]
 CSRC = os.path.join(ROOT, "graph_transformer_sparse_amd", "csrc")
 
 
-def byte_model(cfg, R, M, E, M_nz):
+def byte_model(cfg, R, M, E, M_nz, reads_y):
+    """Algorithmic bytes of each kernel (module docstring); reads_y: the row
+    pass reads Y (with a bias it takes D = <dY, Y> up front)."""
     s = 4 if cfg.dtype == "f32" else 2
     H, D = cfg.heads, cfg.heads * cfg.head_dim
     b = 1 if cfg.bias else 0
+    y = 1 if reads_y else 0
     return {
         "fwd": R * (4 + 2 * D * s + 4 * H) + E * (4 + 2 * D * s + 4 * H * b),
-        "bwd_rows": R * (4 + 3 * D * s + 12 * H) + E * (4 + 2 * D * s + 4 * H * b),
+        "bwd_rows": R * (4 + (3 + y) * D * s + 12 * H) + E * (4 + 2 * D * s + 8 * H * b),
         "bwd_cols": M * (4 + 2 * D * s) + M_nz * 2 * D * s
-        + E * (4 + 2 * D * s + 8 * H + (4 + 8 * H) * b),
+        + E * (4 + 2 * D * s + 8 * H + (4 + 4 * H) * b),
     }
+
+
+def aux_model(cfg, R, E):
+    """Bytes of the pass that finishes dbias from its staged values (with a
+    bias): every staged value read and written back once, plus two floats
+    per row and head.  Not part of the step's algorithmic bytes above (the
+    method itself needs no staging), but a kernel of the step."""
+    if not cfg.bias:
+        return {}
+    return {"bwd_dbias": E * 8 * cfg.heads + R * 8 * cfg.heads}
 
 
 # the sources that decide what the kernels read and write: the kernels, their
@@ -120,37 +146,26 @@ def _compare_lse(got, ref, rtol):
     return {"max_err_over_bound": ratio, "ok": bool(same and ratio <= 1.0)}
 
 
-def cpu_baseline(P, budget_s: float, gpu_rows=None):
-    """The oracle (fp64, OpenMP) on a row block of the same workload whose
-    size is picked so the run takes about budget_s seconds.
-
-    gpu_rows(k, e), if given, returns the GPU's outputs of the timed run for
-    the first k rows (Y, lse, dQ, and dbias of their e edges; dK and dV when
-    k covers every row); they are compared with the oracle's outputs on the
-    same block, at the tolerance of the parity tests, and the verdict is
-    reported beside the timing."""
+def cpu_baseline(P, budget_s: float):
+    """The oracle (fp64, OpenMP) timed on a row block of the same workload
+    whose size is picked so the run takes about budget_s seconds."""
     from oracle import oracle as O
     cfg = P.cfg
     # the oracle works in float64: widen the inputs once, outside the timing
     Q, K, V, dY = (np.ascontiguousarray(x, dtype=np.float64) for x in (P.Q, P.K, P.V, P.dY))
     B = None if P.bias is None else np.ascontiguousarray(P.bias, dtype=np.float64)
 
-    # calibrate on a small row block, then size the measured block
-    def block(k):
+    def run(k):
         ip = P.indptr[: k + 1]
         e = int(ip[-1])
-        return ip, P.indices[:e], (B[:e] if B is not None else None), e
-
-    def run(k, mag=None):
-        ip, ix, bias, e = block(k)
+        ix, bias = P.indices[:e], (B[:e] if B is not None else None)
         q, dy = np.ascontiguousarray(Q[:k]), np.ascontiguousarray(dY[:k])
         t = time.perf_counter()
-        out = O.fwd(ip, ix, cfg.n_cols, q, K, V, bias, P.scale, mag=mag)
-        out += O.bwd(ip, ix, cfg.n_cols, q, K, V, dy, bias, P.scale, mag=mag)
-        if mag is not None:
-            return out
+        O.fwd(ip, ix, cfg.n_cols, q, K, V, bias, P.scale)
+        O.bwd(ip, ix, cfg.n_cols, q, K, V, dy, bias, P.scale)
         return time.perf_counter() - t, e
 
+    # calibrate on a small row block, then size the measured block
     def sized(budget):
         R = cfg.n_rows
         k = min(R, 4096)
@@ -189,31 +204,7 @@ def cpu_baseline(P, budget_s: float, gpu_rows=None):
     t = time.perf_counter()
     O.transpose(P.indptr, P.indices, cfg.n_cols)
     out["transpose_s"] = time.perf_counter() - t
-    if gpu_rows is not None:
-        out["parity"] = parity_on_block(P, k, e, run, gpu_rows)
     return out
-
-
-def parity_on_block(P, k, e, run, gpu_rows):
-    """The oracle's outputs on rows 0..k-1 (one more, untimed run that also
-    returns the magnitudes of the sums) against the GPU's outputs there."""
-    cfg, rtol = P.cfg, RTOL[P.cfg.dtype]
-    mag = {}
-    Y, lse, dQ, dK, dV, dB = run(k, mag)
-    g = gpu_rows(k, e)
-    rep = {"Y": _compare(g["Y"], Y, rtol, mag["Y"]), "lse": _compare_lse(g["lse"], lse, rtol),
-           "dQ": _compare(g["dQ"], dQ, rtol, mag["dQ"])}
-    if dB is not None:
-        rep["dbias"] = _compare(g["dbias"], dB, rtol)
-    if k == cfg.n_rows:
-        rep["dK"] = _compare(g["dK"], dK, rtol, mag["dK"])
-        rep["dV"] = _compare(g["dV"], dV, rtol, mag["dV"])
-    what = "Y, lse, dQ" + (", dbias" if dB is not None else "")
-    what += ", dK, dV (every row in the block)" if k == cfg.n_rows else \
-        " (dK, dV need every row; compared by the tests)"
-    return {"verdict": "pass" if all(r["ok"] for r in rep.values()) else "FAIL",
-            "rtol": rtol, "compared": f"{what} of rows 0..{k - 1} from the timed run",
-            "tensors": rep}
 
 
 def cpu_model() -> str:
@@ -227,15 +218,62 @@ def cpu_model() -> str:
     return "unknown"
 
 
+SUITE = ["tiny", "mid", "large", "shard", "hub"]   # the last one is the headline
+
+
+def arith_dtype(storage: str) -> str:
+    """The type the attention kernels compute in: float32 for either storage
+    type (bf16 inputs are widened exactly, sums run in float32)."""
+    return {"f32": "f32", "bf16": "f32"}[storage]
+
+
+def unique_bytes(cfg, R, M, E, reads_y):
+    """Compulsory bytes of one step: every array the two calls read or write,
+    counted once per call (a lower bound on HBM traffic; gathers that come
+    back from HBM more than once are what separates the kernels from it).
+      forward : CSR (indptr, indices), Q, K, V, bias in; Y, lse out
+      backward: CSR, its transpose (indptr_t, indices_t, perm), Q, K, V, dY,
+                lse, bias (and Y when the row pass reads it) in; dQ, dK, dV,
+                dbias out; the row statistics written once and read once."""
+    s = 4 if cfg.dtype == "f32" else 2
+    H, D = cfg.heads, cfg.heads * cfg.head_dim
+    b = 1 if cfg.bias else 0
+    csr = 4 * (R + 1) + 4 * E
+    csr_t = 4 * (M + 1) + 8 * E
+    fwd = csr + R * D * s + 2 * M * D * s + 4 * E * H * b + R * D * s + 4 * R * H
+    bwd = (csr + csr_t + (2 + (1 if reads_y else 0)) * R * D * s + 2 * M * D * s + 4 * R * H
+           + 4 * E * H * b + R * D * s + 2 * M * D * s + 4 * E * H * b + 2 * 8 * R * H)
+    return fwd + bwd
+
+
+def counter_record(workload: str):
+    """Counter-measured bytes (FETCH_SIZE + WRITE_SIZE, calibrated) of one
+    step's three main kernels from the committed rocprofv3 records of this
+    workload -- a stored record, used only if every one was taken on the
+    current kernel sources (the merges, under 0.3 % of a step, have no
+    record)."""
+    per = {}
+    for k in ("fwd", "bwd_rows", "bwd_cols"):
+        v = traffic_record(k, workload)
+        if v is None:
+            return None
+        per[k] = v
+    return {"bytes_per_step": sum(per.values()), "per_kernel": per,
+            "source": f"profiles/traffic_{{fwd,bwd_rows,bwd_cols}}_{workload}.txt",
+            "source_hash": kernel_source_hash(), "stored": True}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--config", default="mid",
-                    choices=["tiny", "mid", "large", "hub", "shard"])
+    ap.add_argument("--config", default=None, choices=SUITE,
+                    help="measure one workload only (default: all five, the hub workload "
+                         "as the headline and the others in detail.configs)")
     ap.add_argument("--cpu-budget", type=float, default=15.0,
-                    help="seconds of oracle work for the CPU baseline (0: skip)")
+                    help="seconds of oracle work for the CPU baseline (0: skip it and the "
+                         "parity check of the timed run)")
     ap.add_argument("--layer", action="store_true",
                     help="time a whole layer (dense projections + attention, fwd+bwd) "
                          "instead of the attention alone")
@@ -270,27 +308,81 @@ def main():
               "(the multi-GPU sharding is described, not built)", file=sys.stderr)
         sys.exit(2)
 
+    from graph_transformer_sparse_amd import gtattn as T
+    from graph_transformer_sparse_amd import inputs as I
+
+    T.lib()
+    single = args.config is not None or args.layer or args.head_split or args.hidden or args.nodes
+    if single:
+        cfg = I.CONFIGS[args.config or "mid"]
+        if args.nodes:
+            if cfg.name != "mid" or args.nodes < 2 or args.nodes & (args.nodes - 1):
+                sys.exit("--nodes takes a power of two, with the mid workload")
+            cfg = dataclasses.replace(cfg, n_rows=args.nodes, n_cols=args.nodes,
+                                      desc=f"{cfg.desc}; {args.nodes} nodes")
+        if args.hidden:
+            if args.hidden % cfg.heads:
+                sys.exit(f"--hidden {args.hidden} is not a multiple of the {cfg.heads} heads")
+            cfg = dataclasses.replace(cfg, head_dim=args.hidden // cfg.heads,
+                                      desc=f"{cfg.desc}; hidden {args.hidden}")
+        if args.layer:
+            return layer_bench(args, cfg)
+        if args.head_split:
+            return head_split_bench(args, cfg)
+        plan = [cfg]
+    else:
+        plan = [I.CONFIGS[n] for n in SUITE]
+    t_all = time.perf_counter()
+    details = {}
+    for k, cfg in enumerate(plan):
+        head = k == len(plan) - 1
+        print(f"bench: {cfg.name} ({'headline' if head else 'detail'})", file=sys.stderr,
+              flush=True)
+        r = run_workload(args, cfg, headline=head)
+        if not head:
+            details[cfg.name] = summary(r)
+    line = r["line"]
+    if details:
+        line["detail"]["configs"] = details
+    line["detail"]["bench_wall_s"] = time.perf_counter() - t_all
+    bad = [n for n, d in [(cfg.name, summary(r))] + list(details.items())
+           if d.get("parity") and d["parity"] != "pass"]
+    if bad:
+        print(f"bench: the GPU outputs of the timed run do NOT match the oracle on {bad}",
+              file=sys.stderr)
+    print(json.dumps(line), flush=True)
+
+
+def summary(r):
+    """The per-workload entry of detail.configs."""
+    line = r["line"]
+    d = line["detail"]
+    par = r.get("parity")
+    return {"workload": line["config"]["workload"], "nnz": line["config"]["nnz"],
+            "storage": line["config"]["storage"], "bias": line["config"]["bias"],
+            "ms_per_step": line["ms_per_step"], "GEdges_per_s": line["value"],
+            "step_model_GB": d["step_model_GB"], "step_frac": d["step_frac"],
+            "unique_GB": d["unique_GB"], "unique_frac": line["roofline"]["unique_frac"],
+            "counter_frac": line["roofline"]["counter_frac"],
+            "dominant": {"kernel": line["roofline"]["kernel"],
+                         "ms_per_launch": d["kernels"][line["roofline"]["kernel"]]["ms_per_launch"],
+                         "model_GBps": line["roofline"]["achieved"],
+                         "frac": line["roofline"]["frac"]},
+            "kernels_ms": {k: v["ms_per_launch"] for k, v in d["kernels"].items()},
+            "parity": par["verdict"] if par else None,
+            "parity_detail": par}
+
+
+def run_workload(args, cfg, headline: bool):
+    """One workload: generate it, prepare the graph, warm up, time the steps,
+    check the timed run's outputs against the oracle (every output of the
+    whole graph) and, for the headline, time the oracle on a bounded sample.
+    Returns dict(line=<the JSON line of this workload>, parity=...)."""
     import torch
 
     from graph_transformer_sparse_amd import gtattn as T
     from graph_transformer_sparse_amd import inputs as I
 
-    T.lib()
-    cfg = I.CONFIGS[args.config]
-    if args.nodes:
-        if cfg.name != "mid" or args.nodes < 2 or args.nodes & (args.nodes - 1):
-            sys.exit("--nodes takes a power of two, with the mid workload")
-        cfg = dataclasses.replace(cfg, n_rows=args.nodes, n_cols=args.nodes,
-                                  desc=f"{cfg.desc}; {args.nodes} nodes")
-    if args.hidden:
-        if args.hidden % cfg.heads:
-            sys.exit(f"--hidden {args.hidden} is not a multiple of the {cfg.heads} heads")
-        cfg = dataclasses.replace(cfg, head_dim=args.hidden // cfg.heads,
-                                  desc=f"{cfg.desc}; hidden {args.hidden}")
-    if args.layer:
-        return layer_bench(args, cfg)
-    if args.head_split:
-        return head_split_bench(args, cfg)
     t0 = time.perf_counter()
     P = I.make_problem(cfg)
     gen_s = time.perf_counter() - t0
@@ -323,7 +415,7 @@ def main():
 
     def step():
         T.gt_attn_fwd(g, Q, K, V, bias, P.scale, work, Y, lse)
-        T.gt_attn_bwd(g, Q, K, V, lse, dY, bias, P.scale, work, dQ, dK, dV, dbias)
+        T.gt_attn_bwd(g, Q, K, V, Y, lse, dY, bias, P.scale, work, dQ, dK, dV, dbias)
 
     def kernel_times():
         out = {}
@@ -334,7 +426,8 @@ def main():
         return out
 
     M_nz = int(np.count_nonzero(np.diff(T_np(g.indptr_t))))
-    model = byte_model(cfg, R, M, E, M_nz)
+    reads_y = T.bwd_reads_y(bias is not None)
+    model = byte_model(cfg, R, M, E, M_nz, reads_y)
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
@@ -376,20 +469,25 @@ def main():
     ms_step = elapsed * 1e3 / args.steps
     per_step = sorted(marks[i].elapsed_time(marks[i + 1]) for i in range(args.steps))
     kern[dominant] = kernel_times()[dominant]
-    for k in model:
+    for k, byt in list(model.items()) + list(aux_model(cfg, R, E).items()):
         if k in kern:
-            kern[k]["model_GB"] = model[k] / 1e9
-            kern[k]["GBps"] = model[k] / (kern[k]["ms_per_launch"] * 1e-3) / 1e9
+            kern[k]["model_GB"] = byt / 1e9
+            kern[k]["GBps"] = byt / (kern[k]["ms_per_launch"] * 1e-3) / 1e9
+            kern[k]["frac"] = kern[k]["GBps"] / HBM_PEAK_GBS
     ach = kern[dominant]["GBps"]
     # the committed counter records are for each workload's own shape and size
-    traffic = None if (args.hidden or args.nodes) else traffic_record(dominant, cfg.name)
+    shaped = not (args.hidden or args.nodes)
+    traffic = traffic_record(dominant, cfg.name) if shaped else None
+    counters = counter_record(cfg.name) if shaped else None
     total_model = sum(model.values())
+    uniq = unique_bytes(cfg, R, M, E, reads_y)
+    step_s = ms_step * 1e-3
     graph_ms = graph_replay_ms(step, args.steps)
     copy_gbps = copy_rate_gbps()
 
     line = {
         "metric": "GEdges/s fused sparse-attn fwd+bwd, 1 MI355X; achieved HBM GB/s vs peak",
-        "value": E / (ms_step * 1e-3) / 1e9,
+        "value": E / step_s / 1e9,
         "unit": "GEdges/s",
         "n_gpus": 1,
         "steps": args.steps,
@@ -398,18 +496,25 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "f32",
+        "dtype": arith_dtype(cfg.dtype),
         "data": "synthetic (seeded generators standing in for the pages' graphs)",
         "config": {"workload": f"{cfg.name}: {cfg.desc}", "nodes": R, "kv_nodes": M, "nnz": E,
                    "heads": H, "head_dim": dh, "storage": cfg.dtype, "bias": cfg.bias,
                    "parallelism": "single GPU"},
         "roofline": {"bound": "hbm", "kernel": dominant, "achieved": ach, "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": ach / HBM_PEAK_GBS,
-                     "traffic": traffic},
+                     "traffic": traffic,
+                     # the step's compulsory bytes (every array once) over the step time
+                     "unique_frac": uniq / step_s / 1e9 / HBM_PEAK_GBS,
+                     # the step's counter-measured bytes (stored record) over the step time
+                     "counter_frac": (counters["bytes_per_step"] / step_s / 1e9 / HBM_PEAK_GBS
+                                      if counters else None)},
         "cpu_baseline": None,
         "detail": {"step_model_GB": total_model / 1e9,
-                   "step_GBps": total_model / (ms_step * 1e-3) / 1e9,
-                   "step_frac": total_model / (ms_step * 1e-3) / 1e9 / HBM_PEAK_GBS,
+                   "step_GBps": total_model / step_s / 1e9,
+                   "step_frac": total_model / step_s / 1e9 / HBM_PEAK_GBS,
+                   "unique_GB": uniq / 1e9,
+                   "counters": counters,
                    "step_ms_events": {"mean": sum(per_step) / len(per_step),
                                       "min": per_step[0],
                                       "median": per_step[len(per_step) // 2]},
@@ -421,20 +526,49 @@ def main():
                    "copy_GBps": copy_gbps,
                    "frac_of_copy": ach / copy_gbps if copy_gbps else None},
     }
+    parity = None
     if args.cpu_budget > 0:
-        def gpu_rows(k, e):
-            f64 = lambda t: t.float().cpu().numpy().astype(np.float64)
-            out = {"Y": f64(Y[:k]), "lse": f64(lse[:k]), "dQ": f64(dQ[:k])}
-            if dbias is not None:
-                out["dbias"] = f64(dbias[:e])
-            if k == R:
-                out["dK"], out["dV"] = f64(dK), f64(dV)
-            return out
-        line["cpu_baseline"] = cpu_baseline(P, args.cpu_budget, gpu_rows)
-        if line["cpu_baseline"]["parity"]["verdict"] != "pass":
-            print("bench: the GPU outputs of the timed run do NOT match the oracle",
-                  file=sys.stderr)
-    print(json.dumps(line), flush=True)
+        # the outputs of the last timed step (the graph replays after it
+        # recompute them bitwise), then free the device
+        f64 = lambda t: t.float().cpu().numpy().astype(np.float64)
+        got = {"Y": f64(Y), "lse": f64(lse), "dQ": f64(dQ), "dK": f64(dK), "dV": f64(dV),
+               "dbias": f64(dbias) if dbias is not None else None}
+        del Q, K, V, dY, bias, Y, lse, dQ, dK, dV, dbias, work, g, indptr, indices
+        torch.cuda.empty_cache()
+        t0 = time.perf_counter()
+        parity = parity_full(P, got)
+        parity["oracle_s"] = time.perf_counter() - t0
+        del got
+        line["detail"]["parity"] = parity
+        if headline:
+            line["cpu_baseline"] = cpu_baseline(P, args.cpu_budget)
+            line["cpu_baseline"]["parity"] = {k: parity[k] for k in ("verdict", "rtol", "compared")}
+    return {"line": line, "parity": parity}
+
+
+def parity_full(P, got):
+    """The oracle's outputs on the whole graph (with the magnitudes of its
+    sums) against the GPU's outputs of the timed run, at the tests'
+    tolerance: every row of Y, lse, dQ (and dbias), every column of dK, dV."""
+    from oracle import oracle as O
+    cfg, rtol = P.cfg, RTOL[P.cfg.dtype]
+    M = cfg.n_cols
+    mag = {}
+    Q, K, V, dY = (np.ascontiguousarray(x, dtype=np.float64) for x in (P.Q, P.K, P.V, P.dY))
+    B = None if P.bias is None else np.ascontiguousarray(P.bias, dtype=np.float64)
+    rY, rl = O.fwd(P.indptr, P.indices, M, Q, K, V, B, P.scale, mag=mag)
+    rep = {"Y": _compare(got["Y"], rY, rtol, mag.pop("Y")),
+           "lse": _compare_lse(got["lse"], rl, 1e-5 if cfg.dtype == "f32" else 1e-4)}
+    del rY, rl
+    rQ, rK, rV, rB = O.bwd(P.indptr, P.indices, M, Q, K, V, dY, B, P.scale, mag=mag)
+    rep["dQ"] = _compare(got["dQ"], rQ, rtol, mag.pop("dQ"))
+    rep["dK"] = _compare(got["dK"], rK, rtol, mag.pop("dK"))
+    rep["dV"] = _compare(got["dV"], rV, rtol, mag.pop("dV"))
+    if rB is not None:
+        rep["dbias"] = _compare(got["dbias"], rB, rtol)
+    what = "Y, lse, dQ" + (", dbias" if rB is not None else "") + " of every row, dK, dV of every column"
+    return {"verdict": "pass" if all(r["ok"] for r in rep.values()) else "FAIL",
+            "rtol": rtol, "compared": f"{what}, from the timed run", "tensors": rep}
 
 
 def copy_rate_gbps(mib: int = 1024, reps: int = 10):
@@ -555,7 +689,7 @@ def layer_bench(args, cfg):
         Q, K, V = timed("proj_qkv", lambda: T.gt_proj_qkv(Xd, Wd["q"], Wd["k"], Wd["v"]))
         T.gt_attn_fwd(g, Q.view(shp), K.view(shp), V.view(shp), bias, P.scale, work, Y, lse)
         timed("proj_out", lambda: T.gt_proj_out(Xd, Wd["o"], Y.view(n, d)))
-        T.gt_attn_bwd(g, Q.view(shp), K.view(shp), V.view(shp), lse, dZd.view(shp), bias,
+        T.gt_attn_bwd(g, Q.view(shp), K.view(shp), V.view(shp), Y, lse, dZd.view(shp), bias,
                       P.scale, work, dQ, dK, dV, dbias)
         args4 = (dZd, dQ.view(n, d), dK.view(n, d), dV.view(n, d))
         timed("proj_bwd_data", lambda: T.gt_proj_bwd_data(*args4, Wd["o"], Wd["q"], Wd["k"], Wd["v"]))
@@ -584,7 +718,7 @@ def layer_bench(args, cfg):
     ev.clear()
     s = 4 if cfg.dtype == "f32" else 2
     M_nz = int(np.count_nonzero(np.diff(T_np(g.indptr_t))))
-    model = byte_model(cfg, n, n, E, M_nz)
+    model = byte_model(cfg, n, n, E, M_nz, T.bwd_reads_y(bias is not None))
     pm = proj_model(n, d, s)
     for k, (byt, flops) in pm.items():
         t = kern[k]["ms_per_launch"] * 1e-3
@@ -636,7 +770,27 @@ def layer_bench(args, cfg):
         "detail": {"kernels": kern, "input_gen_s": gen_s,
                    "kernel_source_hash": kernel_source_hash()},
     }
+    if args.cpu_budget > 0:
+        line["cpu_baseline"] = layer_cpu_baseline(P, X, W, dZ)
     print(json.dumps(line), flush=True)
+
+
+def layer_cpu_baseline(P, X, W, dZ):
+    """The layer oracle (float64; numpy's matmul for the projections, the C
+    oracle with OpenMP for the attention) on the whole workload, once."""
+    from oracle import layer as L
+    from oracle import oracle as O
+    cfg = P.cfg
+    store = "bf16" if cfg.dtype == "bf16" else None
+    t = time.perf_counter()
+    L.layer_fwd(P.indptr, P.indices, X, W, cfg.heads, P.bias, P.scale, store)
+    L.layer_bwd(P.indptr, P.indices, X, W, cfg.heads, dZ, P.bias, P.scale, store)
+    dt = time.perf_counter() - t
+    return {"value": P.nnz / dt / 1e9, "unit": "GEdges/s", "cores": O.threads(),
+            "kind": "oracle",
+            "sample": (f"the whole {cfg.name} layer once: forward and backward in float64 "
+                       f"(projections by numpy matmul, attention by the C oracle) in {dt:.1f} s"),
+            "cpu": cpu_model()}
 
 
 def head_split_bench(args, cfg):
@@ -700,7 +854,8 @@ def head_split_bench(args, cfg):
                   "(repack + per-slice attention), 1 MI355X",
         "value": P.nnz / (ms_step * 1e-3) / 1e9, "unit": "GEdges/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms_step,
-        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": arith_dtype(cfg.dtype),
         "data": "synthetic (seeded generators standing in for the pages' graphs)",
         "config": {"workload": f"{cfg.name}: {cfg.desc}", "parts": parts, "nodes": R,
                    "heads": H, "head_dim": dh, "storage": cfg.dtype, "bias": cfg.bias,

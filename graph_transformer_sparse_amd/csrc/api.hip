@@ -22,9 +22,9 @@ gt_status launch_fwd(const gt_graph *g, int heads, int head_dim, gt_dtype dt, fl
                      float *lse, float *part, hipStream_t st);
 gt_status launch_bwd(const gt_graph *g, int heads, int head_dim, gt_dtype dt, float scale,
                      const void *Q, const void *K, const void *V, const float *bias,
-                     const float *lse, const void *dY, void *dQ, void *dK,
-                     void *dV, float *dbias, float *rowstat, float *part_rows, float *part_cols,
-                     hipStream_t st);
+                     const void *Y, const float *lse, const void *dY, void *dQ, void *dK,
+                     void *dV, float *dbias, float *rowstat, float *fixstat, float *part_rows,
+                     float *part_cols, hipStream_t st);
 
 static thread_local char g_err[512];
 
@@ -52,7 +52,8 @@ Prof &prof() {
   return p;
 }
 const char *const kPkNames[PK_COUNT] = {"fwd",      "fwd_merge",      "bwd_rows",
-                                        "bwd_rows_merge", "bwd_cols", "bwd_cols_merge"};
+                                        "bwd_rows_merge", "bwd_cols", "bwd_cols_merge",
+                                        "bwd_dbias"};
 }  // namespace
 
 int prof_begin(ProfKernel k, hipStream_t s) {
@@ -89,8 +90,8 @@ using namespace gt;
 namespace {
 
 struct WorkLayout {
-  size_t part_fwd;                        // forward
-  size_t rowstat, part_rows, part_cols;   // backward
+  size_t part_fwd;                                 // forward
+  size_t rowstat, fixstat, part_rows, part_cols;   // backward
   size_t fwd_total, bwd_total, total;
 };
 
@@ -103,7 +104,8 @@ WorkLayout work_layout(const gt_graph *g, int heads, int head_dim) {
   w.part_fwd = 0;
   w.fwd_total = align256(sr * (size_t)fwd_slot_floats(D, heads) * sizeof(float));
   w.rowstat = 0;
-  w.part_rows = align256((size_t)g->n_rows * heads * 2 * sizeof(float));
+  w.fixstat = align256((size_t)g->n_rows * heads * 2 * sizeof(float));
+  w.part_rows = w.fixstat + align256((size_t)g->n_rows * heads * 2 * sizeof(float));
   w.part_cols = w.part_rows + align256(sr * (size_t)rows_slot_floats(D, heads) * sizeof(float));
   w.bwd_total = w.part_cols + align256(sc * (size_t)cols_slot_floats(D, heads) * sizeof(float));
   w.total = std::max<size_t>(std::max(w.fwd_total, w.bwd_total), 256);
@@ -172,8 +174,8 @@ extern "C" gt_status gt_attn_fwd(const gt_graph *g, int32_t heads, int32_t head_
 
 extern "C" gt_status gt_attn_bwd(const gt_graph *g, int32_t heads, int32_t head_dim, gt_dtype dt,
                                  float scale, const void *Q, const void *K, const void *V,
-                                 const float *bias, const float *lse, const void *dY, void *dQ,
-                                 void *dK, void *dV, float *dbias,
+                                 const float *bias, const void *Y, const float *lse,
+                                 const void *dY, void *dQ, void *dK, void *dV, float *dbias,
                                  void *work, size_t work_bytes, void *stream) {
   clear_error();
   TRY(check_common(g, heads, head_dim, dt));
@@ -183,6 +185,7 @@ extern "C" gt_status gt_attn_bwd(const gt_graph *g, int32_t heads, int32_t head_
   TRY(check_feat(Q, "Q", rows));
   TRY(check_feat(K, "K", cols));
   TRY(check_feat(V, "V", cols));
+  TRY(check_feat(Y, "Y", rows && bias != nullptr));
   TRY(check_feat(dY, "dY", rows));
   TRY(check_feat(dQ, "dQ", rows));
   TRY(check_feat(dK, "dK", cols));
@@ -197,9 +200,10 @@ extern "C" gt_status gt_attn_bwd(const gt_graph *g, int32_t heads, int32_t head_
   if (work_bytes < w.bwd_total)
     return fail(GT_E_WORKSPACE, "work has %zu bytes, needs %zu", work_bytes, w.bwd_total);
   char *wb = (char *)work;
-  return launch_bwd(g, heads, head_dim, dt, scale, Q, K, V, bias, lse, dY, dQ, dK, dV, dbias,
-                    (float *)(wb + w.rowstat), (float *)(wb + w.part_rows),
-                    (float *)(wb + w.part_cols), (hipStream_t)stream);
+  return launch_bwd(g, heads, head_dim, dt, scale, Q, K, V, bias, Y, lse, dY, dQ, dK, dV, dbias,
+                    (float *)(wb + w.rowstat), (float *)(wb + w.fixstat),
+                    (float *)(wb + w.part_rows), (float *)(wb + w.part_cols),
+                    (hipStream_t)stream);
 }
 
 extern "C" gt_status gt_prof_enable(int32_t kernel_mask) {
@@ -258,4 +262,4 @@ extern "C" const char *gt_status_str(gt_status s) {
 
 extern "C" const char *gt_last_error(void) { return g_err; }
 
-extern "C" int32_t gt_version(void) { return 101; }
+extern "C" int32_t gt_version(void) { return 102; }

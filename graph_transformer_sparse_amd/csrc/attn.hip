@@ -378,13 +378,16 @@ __global__ __launch_bounds__(BLOCK) void k_fwd(FwdArgs a) {
       sc[u] = ok[u] ? d : -INFINITY;
       mn = fmaxf(mn, sc[u]);
     }
-    const float alpha = fast_exp2(st.m - mn);
+    // ms: the running maximum, or 0 while every score seen is -inf (edges
+    // masked by a -inf bias), so that 2^(-inf - ms) = 0 instead of NaN
+    const float ms = mn > -INFINITY ? mn : 0.f;
+    const float alpha = fast_exp2(st.m - ms);
     st.l *= alpha;
 #pragma unroll
     for (int c = 0; c < N; ++c) st.acc[c] *= alpha;
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      const float p = fast_exp2(sc[u] - mn);
+      const float p = fast_exp2(sc[u] - ms);
       float vx[N];
       unpack(vr[u], vx);
       st.l += p;
@@ -451,39 +454,111 @@ __global__ __launch_bounds__(BLOCK) void k_fwd_merge(FwdArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// backward, row pass over A: dQ and the per-row (lse2, D) statistics
+// backward, row pass over A: dQ, the per-row (lse2, D) statistics and, with a
+// bias, the staged per-edge values dbias is finished from
 //
-// With U_e = p_e / L, p_e = 2^(s2_e - lse2_i) recomputed from the forward's
-// log-sum-exp and L = sum_e p_e (1 up to the rounding of lse), and
-// dU_e = <dY_i, V_j>, the row term is D_i = sum_e U_e dU_e and
-// dQ_i = scale sum_e U_e (dU_e - D_i) K_j.  One pass over the row's edges
-// accumulates, around a shift c (the dU of the first edge a lane group sees),
+// The weights are recomputed from the forward's log-sum-exp: p_e =
+// 2^(s2_e - lse2_i), L = sum_e p_e (1 up to the rounding of lse), and
+// U_e = p_e / L.  With dU_e = <dY_i, V_j>, the row term is
+// D_i = sum_e U_e dU_e and dQ_i = scale sum_e U_e (dU_e - D_i) K_j.  One pass
+// over the row's edges accumulates, around a shift c,
 //   L = sum p,  S = sum p (dU - c),  A1 = sum p (dU - c) K,  A2 = sum p K,
-// and then D = c + S / L and dQ = scale (A1 - (S / L) A2) / L.  Dividing by L
-// makes the weights sum to 1 whatever the rounding of lse (the column pass
+// and then D = c + S / L and dQ = scale (A1 - (S / L) A2) / L.  Dividing by
+// L makes the weights sum to 1 whatever the rounding of lse (the column pass
 // gets lse2 + log2(L) so that its weights are the same U_e); the shift keeps
-// the subtraction small, and a row with one edge gets dQ = 0 and D = dU
-// exactly.  Two partial states combine at the shift of the first non-empty
-// one: S = S_a + S_b + (c_b - c_a) L_b, A1 = A1_a + A1_b + (c_b - c_a) A2_b.
+// the subtraction small.  Two partial states combine at the shift of the
+// first non-empty one: S = S_a + S_b + (c_b - c_a) L_b,
+// A1 = A1_a + A1_b + (c_b - c_a) A2_b.
+//
+// The shift.  Without a bias, c is the dU of the first edge a lane group
+// sees (a row with one edge then gets dQ = 0 and D = dU exactly).  With a
+// bias, c = <dY_i, Y_i> from the forward's output, the same for every lane
+// group and piece of the row.  That is D itself up to the rounding of the
+// stored Y (2^-9 relative for bf16), so each edge's
+//   w_e = p_e (dU_e - c) = L dS_e + p_e (D_i - c)
+// is known as soon as the edge is, and is staged in the dbias array in CSR
+// edge order (together with p_e: the pair as two bf16 halves for bf16
+// storage, w_e alone as float32 for float32 storage, where D - c is at the
+// float32 rounding level).  A streaming pass (k_bwd_dbias) then finishes
+//   dbias_e = dS_e = (w_e - p_e (D_i - c)) / L
+// in place, from the per-row (D - c, 1 / L).  So dbias leaves in whole
+// lines, and the column pass over the transpose touches it not at all (its
+// scattered 16-byte writes cost more than the staging and the finishing
+// pass together).
 // ---------------------------------------------------------------------------
 struct BwdArgs {
   Sched rows, cols;
+  const int32_t *indptr;  // CSR row pointer
+  int64_t n_rows, nnz;
   const int32_t *idx;     // CSR columns
   const int32_t *idx_t;   // CSR^T source rows
   const int32_t *perm;    // CSR^T -> CSR edge id
-  const void *Q, *K, *V, *dY;
+  const void *Q, *K, *V, *Y, *dY;
   const float *lse, *bias;
   void *dQ, *dK, *dV;
   float *dbias;
   float2 *rowstat;        // [R][H] (lse * log2(e) + log2(L), D)
+  float2 *fixstat;        // [R][H] (D - c, 1 / L), with a bias
   float *part_rows;       // [slots][rows_slot_floats] states of split-row pieces
   float *part_cols;       // [slots][cols_slot_floats] states of split-column pieces
   float qscale, scale;
 };
 
+// <dY_i, Y_i> for the head of this lane (every lane of the row's group gets
+// it), in the same operation order as an edge's dU = <dY_i, V_j>.
+template <typename T, int HL, int H>
+__device__ inline float row_shift(const BwdArgs &a, int64_t row, int gl,
+                                  const float (&dy)[Vec<T>::N]) {
+  constexpr int N = Vec<T>::N, D = HL * H * N;
+  float y[N];
+  Vec<T>::load((const T *)a.Y + row * D + gl * N, y);
+  float d = 0.f;
+#pragma unroll
+  for (int c = 0; c < N; ++c) d = fmaf(dy[c], y[c], d);
+  return group_sum<HL>(d);
+}
+
+// The staged value of one edge and head: (p, w) as two bf16 halves, or w
+// as float32 (see above); and its inverse, used by k_bwd_dbias.
+template <typename T> __device__ inline float stage(float p, float w);
+template <> __device__ inline float stage<float>(float, float w) { return w; }
+template <> __device__ inline float stage<bf16_t>(float p, float w) {
+  return __uint_as_float((f32_to_bf16_bits(p) << 16) | f32_to_bf16_bits(w));
+}
+template <typename T> __device__ inline float unstage(float v, float dc, float inv);
+template <> __device__ inline float unstage<float>(float v, float, float inv) { return v * inv; }
+template <> __device__ inline float unstage<bf16_t>(float v, float dc, float inv) {
+  const uint32_t u = __float_as_uint(v);
+  const float p = __uint_as_float(u & 0xffff0000u), w = __uint_as_float(u << 16);
+  return (w - p * dc) * inv;
+}
+
+// Store one round's staged values (edges e + u gstep, u < U): lane r of a
+// head's HL lanes stores that head's value of edge r (and r + HL, ...), so a
+// round's values leave in one store instruction.
+template <int U, int HL, int H>
+__device__ inline void stage_store(float *dbias, int64_t e, int gstep, int gl, int h,
+                                   const float (&sv)[U], const bool (&ok)[U]) {
+#pragma unroll
+  for (int u0 = 0; u0 < U; u0 += HL) {
+    const int u = u0 + gl % HL;
+    if (u < U) {
+      float v = sv[0];
+      bool w = ok[0];
+#pragma unroll
+      for (int k = 1; k < U; ++k)
+        if (u == k) {
+          v = sv[k];
+          w = ok[k];
+        }
+      if (w) dbias[(e + (int64_t)u * gstep) * H + h] = v;
+    }
+  }
+}
+
 // dQ and the row statistics of one row from its state (all lanes of the
 // row's group; lane gl holds channels [gl*N, gl*N + N)).
-template <typename T, int HL, int H>
+template <typename T, int HL, int H, bool BIAS>
 __device__ inline void finish_row(const BwdArgs &a, int64_t row, int gl, int h, float lse2,
                                   const RowState<Vec<T>::N> &st) {
   constexpr int N = Vec<T>::N, D = HL * H * N;
@@ -493,9 +568,11 @@ __device__ inline void finish_row(const BwdArgs &a, int64_t row, int gl, int h, 
 #pragma unroll
   for (int c = 0; c < N; ++c) g[c] = a.scale * ((st.a1[c] - ds * st.a2[c]) * inv);
   Vec<T>::store((T *)a.dQ + row * D + gl * N, g);
-  if (gl % HL == 0)
+  if (gl % HL == 0) {
     a.rowstat[row * H + h] =
         st.l > 0.f ? make_float2(lse2 + fast_log2(st.l), st.c + ds) : make_float2(-INFINITY, 0.f);
+    if constexpr (BIAS) a.fixstat[row * H + h] = make_float2(ds, inv);
+  }
 }
 
 template <typename T, int HL, int H, int U, bool BIAS>
@@ -512,13 +589,22 @@ __global__ __launch_bounds__(BLOCK) void k_bwd_rows(BwdArgs a) {
 #pragma unroll
   for (int c = 0; c < N; ++c) q[c] *= a.qscale;
   const float lse2 = a.lse[row * H + h] * LOG2E;
+  // lse = -inf: every edge of the row is masked (weight 0 throughout)
+  const bool live = lse2 > -INFINITY;
   RowState<N> st;
   st.init();
+  if constexpr (BIAS) st.c = row_shift<T, HL, H>(a, row, gl, dy);
   const int gstep = wk.wave_item ? RPW : 1;
   int64_t e = (int64_t)wk.eb + (wk.wave_item ? grp : 0);
   int32_t jn[U];
   if (e < wk.ee) round_ids<U>(a.idx, e, wk.ee, gstep, jn);
   bool first = true;
+  // the previous round's staged values (bias): stored after this round's
+  // loads are issued, so that waiting for those loads (the memory counter
+  // is in order) does not also wait for the store
+  float sv[U];
+  bool sok[U];
+  int64_t se = -1;
   for (; e < wk.ee; e += (int64_t)gstep * U) {
     int32_t j[U];
     bool ok[U];
@@ -542,6 +628,9 @@ __global__ __launch_bounds__(BLOCK) void k_bwd_rows(BwdArgs a) {
     }
     const int64_t en = e + (int64_t)gstep * U;
     if (en < wk.ee) round_ids<U>(a.idx, en, wk.ee, gstep, jn);
+    if constexpr (BIAS) {
+      if (se >= 0) stage_store<U, HL, H>(a.dbias, se, gstep, gl, h, sv, sok);
+    }
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       float kx[N], vx[N];
@@ -556,9 +645,13 @@ __global__ __launch_bounds__(BLOCK) void k_bwd_rows(BwdArgs a) {
       s = group_sum<HL>(s);
       du = group_sum<HL>(du);
       if constexpr (BIAS) s += b[u];
-      if (u == 0 && first) st.c = du;   // edge e is valid in every round
-      const float p = ok[u] ? fast_exp2(s - lse2) : 0.f;
+      if (!BIAS && u == 0 && first) st.c = du;   // edge e is valid in every round
+      const float p = (ok[u] && live) ? fast_exp2(s - lse2) : 0.f;
       const float pt = p * (du - st.c);
+      if constexpr (BIAS) {
+        sv[u] = stage<T>(p, pt);
+        sok[u] = ok[u];
+      }
       st.l += p;
       st.s += pt;
 #pragma unroll
@@ -567,7 +660,11 @@ __global__ __launch_bounds__(BLOCK) void k_bwd_rows(BwdArgs a) {
         st.a2[c] = fmaf(p, kx[c], st.a2[c]);
       }
     }
+    if constexpr (BIAS) se = e;
     first = false;
+  }
+  if constexpr (BIAS) {
+    if (se >= 0) stage_store<U, HL, H>(a.dbias, se, gstep, gl, h, sv, sok);
   }
   if (wk.wave_item) {
     wave_combine<RowState<N>, G>(st);
@@ -578,10 +675,10 @@ __global__ __launch_bounds__(BLOCK) void k_bwd_rows(BwdArgs a) {
       return;
     }
   }
-  finish_row<T, HL, H>(a, row, gl, h, lse2, st);
+  finish_row<T, HL, H, BIAS>(a, row, gl, h, lse2, st);
 }
 
-template <typename T, int HL, int H>
+template <typename T, int HL, int H, bool BIAS>
 __global__ __launch_bounds__(BLOCK) void k_bwd_rows_merge(BwdArgs a) {
   constexpr int N = Vec<T>::N, G = HL * H, D = G * N;
   const int lane = threadIdx.x & (WAVE - 1), grp = lane / G, gl = lane % G, h = gl / HL;
@@ -590,11 +687,77 @@ __global__ __launch_bounds__(BLOCK) void k_bwd_rows_merge(BwdArgs a) {
   RowState<N> st;
   if (merge_pieces<RowState<N>, D, H, G, rows_slot_floats(D, H)>(st, a.part_rows, first, nch,
                                                                  threadIdx.x / WAVE, grp, gl, h))
-    finish_row<T, HL, H>(a, row, gl, h, a.lse[row * H + h] * LOG2E, st);
+    finish_row<T, HL, H, BIAS>(a, row, gl, h, a.lse[row * H + h] * LOG2E, st);
+}
+
+// dbias from the staged values, streamed in CSR edge order after the row
+// pass and its merges (when every row's (D - c, 1 / L) is known).  A
+// workgroup takes DB_TILE consecutive edges: two searches give the rows of
+// its first and last edge, the row pointers between them go to LDS, and
+// each group of four values finds its row there (a tile spanning more rows
+// than fit, i.e. many empty rows, searches the global row pointer instead).
+constexpr int DB_THREADS = 256, DB_TILE = 2048, DB_ROWS = 2048;
+
+template <typename T, int H>
+__global__ __launch_bounds__(DB_THREADS) void k_bwd_dbias(const int32_t *indptr, int64_t n_rows,
+                                                           int64_t nnz, const float2 *fixstat,
+                                                           float *dbias) {
+  __shared__ int32_t ip[DB_ROWS + 1];
+  __shared__ int32_t r01[2];
+  const int64_t e0 = (int64_t)blockIdx.x * DB_TILE;
+  const int64_t e1 = std::min<int64_t>(e0 + DB_TILE, nnz);   // exclusive
+  if (threadIdx.x < 2)
+    r01[threadIdx.x] = row_of_edge(indptr, n_rows, (int32_t)(threadIdx.x == 0 ? e0 : e1 - 1));
+  __syncthreads();
+  const int32_t r0 = r01[0];
+  const int64_t nr = (int64_t)r01[1] - r0 + 1;               // rows r0 .. r1
+  const bool local = nr <= DB_ROWS;
+  if (local)
+    for (int64_t k = threadIdx.x; k <= nr; k += DB_THREADS) ip[k] = indptr[r0 + k];
+  __syncthreads();
+  auto row_of = [&](int64_t e) -> int64_t {
+    if (!local) return row_of_edge(indptr, n_rows, (int32_t)e);
+    int lo = 0, hi = (int)nr;            // last k with ip[k] <= e, in [lo, hi)
+    while (hi - lo > 1) {
+      const int mid = (lo + hi) >> 1;
+      if (ip[mid] <= e) lo = mid;
+      else hi = mid;
+    }
+    return r0 + lo;
+  };
+  // values x = e * H + h; e0 * H is a multiple of 4, so a group of four
+  // starts 16-byte aligned; with H >= 4 it belongs to one edge
+  const int64_t x1 = e1 * H;
+  for (int64_t x = e0 * H + 4 * threadIdx.x; x < x1; x += 4 * DB_THREADS) {
+    if (x + 4 <= x1) {
+      float4 v = *reinterpret_cast<const float4 *>(dbias + x);
+      float o[4] = {v.x, v.y, v.z, v.w};
+      if constexpr (H >= 4) {
+        const int64_t rh = row_of(x / H) * H;
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          const float2 f = fixstat[rh + (x + k) % H];
+          o[k] = unstage<T>(o[k], f.x, f.y);
+        }
+      } else {
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          const float2 f = fixstat[row_of((x + k) / H) * H + (x + k) % H];
+          o[k] = unstage<T>(o[k], f.x, f.y);
+        }
+      }
+      *reinterpret_cast<float4 *>(dbias + x) = make_float4(o[0], o[1], o[2], o[3]);
+    } else {
+      for (int64_t y = x; y < x1; ++y) {
+        const float2 f = fixstat[row_of(y / H) * H + y % H];
+        dbias[y] = unstage<T>(dbias[y], f.x, f.y);
+      }
+    }
+  }
 }
 
 // ---------------------------------------------------------------------------
-// backward, column pass over A^T: dK, dV and dbias
+// backward, column pass over A^T: dK and dV
 // ---------------------------------------------------------------------------
 template <typename T, int HL, int H>
 __device__ inline void finish_col(const BwdArgs &a, int64_t col, int gl,
@@ -669,15 +832,13 @@ __global__ __launch_bounds__(BLOCK) void k_bwd_cols(BwdArgs a) {
       s = group_sum<HL>(s);
       du = group_sum<HL>(du);
       if constexpr (BIAS) s += b[u];
-      const float p = ok[u] ? fast_exp2(s - rs[u].x) : 0.f;
+      // rowstat.x = -inf: a row whose every edge is masked (weight 0)
+      const float p = (ok[u] && rs[u].x > -INFINITY) ? fast_exp2(s - rs[u].x) : 0.f;
       const float ds = p * (du - rs[u].y);
 #pragma unroll
       for (int c = 0; c < N; ++c) {
         st.v[c] = fmaf(p, gx[c], st.v[c]);
         st.k[c] = fmaf(ds, qx[c], st.k[c]);
-      }
-      if constexpr (BIAS) {
-        if (ok[u] && gl % HL == 0) a.dbias[(int64_t)eid[u] * H + h] = ds;
       }
     }
   }
@@ -774,7 +935,16 @@ static gt_status run_bwd(const BwdArgs &a, bool bias, hipStream_t st) {
   }
   if (a.rows.n_merges > 0) {
     const int tok = prof_begin(PK_BWD_ROWS_MERGE, st);
-    launch_blocks(k_bwd_rows_merge<T, HL, H>, a, &BwdArgs::rows, a.rows.n_merges, st);
+    if (bias) launch_blocks(k_bwd_rows_merge<T, HL, H, true>, a, &BwdArgs::rows, a.rows.n_merges, st);
+    else launch_blocks(k_bwd_rows_merge<T, HL, H, false>, a, &BwdArgs::rows, a.rows.n_merges, st);
+    prof_end(tok, st);
+    GT_CHECK_LAUNCH();
+  }
+  if (bias && a.nnz > 0) {
+    // at most 2^31 / DB_TILE workgroups: one launch
+    const int tok = prof_begin(PK_BWD_DBIAS, st);
+    k_bwd_dbias<T, H><<<dim3((unsigned)cdiv(a.nnz, DB_TILE)), DB_THREADS, 0, st>>>(
+        a.indptr, a.n_rows, a.nnz, a.fixstat, a.dbias);
     prof_end(tok, st);
     GT_CHECK_LAUNCH();
   }
@@ -893,18 +1063,22 @@ gt_status launch_fwd(const gt_graph *g, int heads, int head_dim, gt_dtype dt, fl
 
 gt_status launch_bwd(const gt_graph *g, int heads, int head_dim, gt_dtype dt, float scale,
                      const void *Q, const void *K, const void *V, const float *bias,
-                     const float *lse, const void *dY, void *dQ, void *dK,
-                     void *dV, float *dbias, float *rowstat, float *part_rows, float *part_cols,
-                     hipStream_t st) {
+                     const void *Y, const float *lse, const void *dY, void *dQ, void *dK,
+                     void *dV, float *dbias, float *rowstat, float *fixstat, float *part_rows,
+                     float *part_cols, hipStream_t st) {
   BwdArgs a;
   a.rows = sched_of(g->rows);
   a.cols = sched_of(g->cols);
+  a.indptr = g->indptr;
+  a.n_rows = g->n_rows;
+  a.nnz = g->nnz;
   a.idx = g->indices;
   a.idx_t = g->indices_t;
   a.perm = g->perm;
   a.Q = Q;
   a.K = K;
   a.V = V;
+  a.Y = Y;
   a.dY = dY;
   a.lse = lse;
   a.bias = bias;
@@ -913,6 +1087,7 @@ gt_status launch_bwd(const gt_graph *g, int heads, int head_dim, gt_dtype dt, fl
   a.dV = dV;
   a.dbias = dbias;
   a.rowstat = reinterpret_cast<float2 *>(rowstat);
+  a.fixstat = reinterpret_cast<float2 *>(fixstat);
   a.part_rows = part_rows;
   a.part_cols = part_cols;
   a.qscale = scale * LOG2E;

@@ -80,6 +80,18 @@ template <int L> __device__ inline float group_sum(float x) {
   return x;
 }
 
+// The row of CSR edge e (0 <= e < nnz): the last r with indptr[r] <= e,
+// which skips empty rows.
+__device__ inline int32_t row_of_edge(const int32_t *indptr, int64_t n_rows, int32_t e) {
+  int64_t lo = 0, hi = n_rows;  // answer in [lo, hi)
+  while (hi - lo > 1) {
+    const int64_t mid = (lo + hi) >> 1;
+    if (indptr[mid] <= e) lo = mid;
+    else hi = mid;
+  }
+  return (int32_t)lo;
+}
+
 // 2^x on the hardware transcendental unit (v_exp_f32); 2^-inf = 0.
 __device__ inline float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 __device__ inline float fast_log2(float x) { return __builtin_amdgcn_logf(x); }

@@ -32,7 +32,7 @@ void clear_error();
 // Per-kernel event timing (gt_prof_enable).  prof_begin returns a token
 // that prof_end closes after the launch.
 enum ProfKernel { PK_FWD = 0, PK_FWD_MERGE, PK_BWD_ROWS, PK_BWD_ROWS_MERGE, PK_BWD_COLS,
-                  PK_BWD_COLS_MERGE, PK_COUNT };
+                  PK_BWD_COLS_MERGE, PK_BWD_DBIAS, PK_COUNT };
 int prof_begin(ProfKernel k, hipStream_t s);
 void prof_end(int token, hipStream_t s);
 

@@ -268,16 +268,6 @@ __global__ void k_col_ptr(const uint32_t *sorted_cols, int64_t nnz, int64_t n_co
 }
 
 // Row of a CSR edge: the last r with indptr[r] <= e (indptr non-decreasing).
-__device__ inline int32_t row_of_edge(const int32_t *indptr, int64_t n_rows, int32_t e) {
-  int64_t lo = 0, hi = n_rows;  // answer in [lo, hi)
-  while (hi - lo > 1) {
-    const int64_t mid = (lo + hi) >> 1;
-    if (indptr[mid] <= e) lo = mid;
-    else hi = mid;
-  }
-  return (int32_t)lo;
-}
-
 // The row of every CSR edge, in edge order.  A workgroup takes ER_TILE
 // consecutive edges: two searches give the rows of its first and last edge,
 // the indptr entries between them go to LDS, and each edge then searches

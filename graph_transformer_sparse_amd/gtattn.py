@@ -82,7 +82,7 @@ def lib():
         "gt_csr_validate": (_i32, [_P, _P, _i64, _i64, _i64, _P, _sz, C.POINTER(_i32), _P]),
         "gt_attn_work_bytes": (_sz, [G, _i32, _i32]),
         "gt_attn_fwd": (_i32, [G, _i32, _i32, _i32, _f32, _P, _P, _P, _P, _P, _P, _P, _sz, _P]),
-        "gt_attn_bwd": (_i32, [G, _i32, _i32, _i32, _f32, _P, _P, _P, _P, _P, _P,
+        "gt_attn_bwd": (_i32, [G, _i32, _i32, _i32, _f32, _P, _P, _P, _P, _P, _P, _P,
                                _P, _P, _P, _P, _P, _sz, _P]),
         "gt_prof_enable": (_i32, [_i32]),
         "gt_prof_reset": (_i32, []),
@@ -315,12 +315,14 @@ def gt_attn_fwd(g: Graph, Q, K, V, bias=None, scale=None, work=None, Y=None, lse
     return Y, lse
 
 
-def gt_attn_bwd(g: Graph, Q, K, V, lse, dY, bias=None, scale=None, work=None,
+def gt_attn_bwd(g: Graph, Q, K, V, Y, lse, dY, bias=None, scale=None, work=None,
                 dQ=None, dK=None, dV=None, dbias=None):
-    """Backward: returns (dQ, dK, dV, dbias); dbias is None without bias."""
+    """Backward: returns (dQ, dK, dV, dbias); dbias is None without bias.
+    Y and lse are the forward's outputs."""
     where = "gt_attn_bwd"
     R, H, dh, dt, dev = _attn_shapes(where, g, Q, K, V, bias)
     scale = dh ** -0.5 if scale is None else float(scale)
+    _tensor(where, "Y", Y, (R, H, dh), dt, dev)
     _tensor(where, "lse", lse, (R, H), torch.float32, dev)
     _tensor(where, "dY", dY, (R, H, dh), dt, dev)
     dQ = torch.empty_like(Q) if dQ is None else dQ
@@ -337,13 +339,20 @@ def gt_attn_bwd(g: Graph, Q, K, V, lse, dY, bias=None, scale=None, work=None,
     _on_gpu(where, g, dev)
     work = _work(g, H, dh, dev, work)
     _check(lib().gt_attn_bwd(C.byref(g.st), H, dh, _dt(Q.dtype), scale, _ptr(Q), _ptr(K),
-                             _ptr(V), _ptr(bias), _ptr(lse), _ptr(dY), _ptr(dQ),
+                             _ptr(V), _ptr(bias), _ptr(Y), _ptr(lse), _ptr(dY), _ptr(dQ),
                              _ptr(dK), _ptr(dV), _ptr(dbias), _ptr(work), work.numel(),
                              _stream(Q.device)), "gt_attn_bwd")
     return dQ, dK, dV, dbias
 
 
-PROF_KERNELS = ["fwd", "fwd_merge", "bwd_rows", "bwd_rows_merge", "bwd_cols", "bwd_cols_merge"]
+def bwd_reads_y(has_bias: bool) -> bool:
+    """Whether gt_attn_bwd reads Y: with a bias its row pass shifts its sums
+    by <dY, Y> (include/gt_attn.h)."""
+    return bool(has_bias)
+
+
+PROF_KERNELS = ["fwd", "fwd_merge", "bwd_rows", "bwd_rows_merge", "bwd_cols", "bwd_cols_merge",
+                "bwd_dbias"]
 
 
 def prof_enable(kernels=True):
@@ -378,15 +387,15 @@ class GTAttnFn(torch.autograd.Function):
         bias = None if bias is None else bias.contiguous()
         Y, lse = gt_attn_fwd(g, Q, K, V, bias, scale)
         ctx.g, ctx.scale = g, scale
-        ctx.save_for_backward(Q, K, V, lse, bias if bias is not None else torch.empty(0))
+        ctx.save_for_backward(Q, K, V, Y, lse, bias if bias is not None else torch.empty(0))
         ctx.has_bias = bias is not None
         return Y
 
     @staticmethod
     def backward(ctx, dY):
-        Q, K, V, lse, bias = ctx.saved_tensors
+        Q, K, V, Y, lse, bias = ctx.saved_tensors
         bias = bias if ctx.has_bias else None
-        dQ, dK, dV, db = gt_attn_bwd(ctx.g, Q, K, V, lse, dY.contiguous(), bias, ctx.scale)
+        dQ, dK, dV, db = gt_attn_bwd(ctx.g, Q, K, V, Y, lse, dY.contiguous(), bias, ctx.scale)
         return None, dQ, dK, dV, db, None
 
 
@@ -492,18 +501,18 @@ class SGALayerFn(torch.autograd.Function):
         Y, lse = gt_attn_fwd(g, Q.view(shp), K.view(shp), V.view(shp), bias, scale)
         Z = gt_proj_out(X, Wo, Y.view(n, d))
         ctx.g, ctx.heads, ctx.scale, ctx.has_bias = g, heads, scale, bias is not None
-        ctx.save_for_backward(X, Wq, Wk, Wv, Wo, Q, K, V, lse,
+        ctx.save_for_backward(X, Wq, Wk, Wv, Wo, Q, K, V, Y, lse,
                               bias if bias is not None else torch.empty(0))
         return Z
 
     @staticmethod
     def backward(ctx, dZ):
-        X, Wq, Wk, Wv, Wo, Q, K, V, lse, bias = ctx.saved_tensors
+        X, Wq, Wk, Wv, Wo, Q, K, V, Y, lse, bias = ctx.saved_tensors
         bias = bias if ctx.has_bias else None
         dZ = dZ.contiguous()
         n, d = X.shape
         shp = (n, ctx.heads, d // ctx.heads)
-        dQ, dK, dV, db = gt_attn_bwd(ctx.g, Q.view(shp), K.view(shp), V.view(shp), lse,
+        dQ, dK, dV, db = gt_attn_bwd(ctx.g, Q.view(shp), K.view(shp), V.view(shp), Y, lse,
                                      dZ.view(shp), bias, ctx.scale)
         dQ, dK, dV = (t.view(n, d) for t in (dQ, dK, dV))
         dX = gt_proj_bwd_data(dZ, dQ, dK, dV, Wo, Wq, Wk, Wv)
@@ -585,7 +594,7 @@ def attn_head_sliced(g: Graph, Q, K, V, dY=None, bias=None, scale=None, parts: i
     dQp, dKp, dVp = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
     dBp = torch.empty_like(b) if b is not None else None
     for r in range(parts):
-        gt_attn_bwd(g, q[r], k[r], v[r], lsep[r], dy[r], br(r), scale, dQ=dQp[r], dK=dKp[r],
+        gt_attn_bwd(g, q[r], k[r], v[r], Yp[r], lsep[r], dy[r], br(r), scale, dQ=dQp[r], dK=dKp[r],
                     dV=dVp[r], dbias=dBp[r] if dBp is not None else None)
     dB = gt_head_merge(dBp) if dBp is not None else None
     return Y, lse, gt_head_merge(dQp), gt_head_merge(dKp), gt_head_merge(dVp), dB

@@ -174,7 +174,9 @@ size_t gt_attn_work_bytes(const gt_graph *g, int32_t heads, int32_t head_dim);
 /* Forward (Eq. 4-5): Y [n_rows, heads, head_dim] in dt, lse [n_rows, heads]
  * float32.  Q is [n_rows, heads, head_dim], K and V [n_cols, heads,
  * head_dim], all dt.  bias (nullable) is [nnz, heads] float32 in CSR edge
- * order.  Z and U are never materialised: the kernel makes one pass over
+ * order; a -inf bias masks its edge (weight 0; a row with every edge masked
+ * gives Y = 0 and lse = -inf, as an empty row), other bias values must be
+ * finite.  Z and U are never materialised: the kernel makes one pass over
  * each row's edges with an online (running max) softmax.
  * Errors: GT_E_NULL, GT_E_DTYPE, GT_E_SHAPE, GT_E_ALIGN, GT_E_WORKSPACE,
  * GT_E_HIP. */
@@ -183,30 +185,38 @@ gt_status gt_attn_fwd(const gt_graph *g, int32_t heads, int32_t head_dim, gt_dty
                       const float *bias, void *Y, float *lse, void *work, size_t work_bytes,
                       void *stream);
 
-/* Backward (Section 2.2): given lse of gt_attn_fwd and the output gradient
- * dY [n_rows, heads, head_dim], writes dQ [n_rows, heads, head_dim], dK, dV
- * [n_cols, heads, head_dim] (all dt, every element written) and, iff bias is
- * given, dbias [nnz, heads] float32 (bias and dbias must both be NULL or both
- * non-NULL; else GT_E_UNSUPPORTED).  The softmax weights are recomputed from
- * lse.  A pass over the rows of A computes the row term
- * D_i = sum_e U_e dU_e and dQ; a pass over the rows of A^T computes dK, dV
- * and dbias.  No output element is written by more than one wavefront and
- * nothing uses atomics.
+/* Backward (Section 2.2): given Y and lse of gt_attn_fwd and the output
+ * gradient dY [n_rows, heads, head_dim], writes dQ [n_rows, heads,
+ * head_dim], dK, dV [n_cols, heads, head_dim] (all dt, every element
+ * written) and, iff bias is given, dbias [nnz, heads] float32 (bias and
+ * dbias must both be NULL or both non-NULL; else GT_E_UNSUPPORTED).  The
+ * softmax weights are recomputed from lse.  A pass over the rows of A
+ * computes dQ and the row term D_i = sum_e U_e dU_e; with a bias it also
+ * stages each edge's score gradient in dbias, in CSR edge order, around the
+ * shift <dY_i, Y_i> (which is why it reads Y), and a streaming pass finishes
+ * dbias in place once D_i is known.  A pass over the rows of A^T computes dK
+ * and dV.  No output element is written by more than one wavefront and
+ * nothing uses atomics.  With bf16 storage dbias carries the rounding of its
+ * bf16 staging (about 2^-9 relative), within the tolerance of bf16 inputs.
+ * Y is read only when bias is given (it may be NULL otherwise).  A -inf bias
+ * masks its edge (weight 0, dbias 0; a row with every edge masked behaves as
+ * an empty row); bias values must otherwise be finite.
  * Errors: as gt_attn_fwd, plus GT_E_UNSUPPORTED. */
 gt_status gt_attn_bwd(const gt_graph *g, int32_t heads, int32_t head_dim, gt_dtype dt,
                       float scale, const void *Q, const void *K, const void *V,
-                      const float *bias, const float *lse, const void *dY, void *dQ, void *dK,
-                      void *dV, float *dbias, void *work, size_t work_bytes, void *stream);
+                      const float *bias, const void *Y, const float *lse, const void *dY,
+                      void *dQ, void *dK, void *dV, float *dbias, void *work,
+                      size_t work_bytes, void *stream);
 
 /* ---- instrumentation and misc ----------------------------------------- */
 
 /* Kernel timing.  Bit k of kernel_mask selects kernel k of "fwd",
- * "fwd_merge", "bwd_rows", "bwd_rows_merge", "bwd_cols", "bwd_cols_merge"
- * (0: timing off, GT_PROF_ALL: all); every launch of a selected kernel is
+ * "fwd_merge", "bwd_rows", "bwd_rows_merge", "bwd_cols", "bwd_cols_merge",
+ * "bwd_dbias" (0: timing off, GT_PROF_ALL: all); every launch of a selected kernel is
  * bracketed by HIP events on its own stream, and gt_prof_query returns the
  * summed device time and the launch count per kernel name since the last
  * gt_prof_reset.  gt_prof_query synchronises the events. */
-#define GT_PROF_ALL 0x3f
+#define GT_PROF_ALL 0x7f
 gt_status gt_prof_enable(int32_t kernel_mask);
 gt_status gt_prof_reset(void);
 gt_status gt_prof_query(const char *kernel, double *total_ms, int64_t *launches);
@@ -214,7 +224,7 @@ gt_status gt_prof_query(const char *kernel, double *total_ms, int64_t *launches)
 const char *gt_status_str(gt_status s);
 /* Detail of the last failed call on this thread ("" if none). */
 const char *gt_last_error(void);
-/* Version of the ABI: 101 (the schedule carries the segment extents `spans`). */
+/* Version of the ABI: 102 (gt_attn_bwd takes the forward's Y). */
 int32_t gt_version(void);
 
 #ifdef __cplusplus

@@ -95,15 +95,18 @@ def test_fwd_argument_checks(L):
 def test_bwd_argument_checks(L):
     g = _fake_graph()
 
-    def bwd(bias=None, dbias=None, dQ=FAKE, nb=1 << 30, heads=4):
+    def bwd(bias=None, dbias=None, dQ=FAKE, nb=1 << 30, heads=4, Y=FAKE):
         return L.gt_attn_bwd(C.byref(g), heads, 32, T.GT_BF16, 0.1, FAKE, FAKE, FAKE, bias,
-                             FAKE, FAKE, dQ, FAKE, FAKE, dbias, FAKE, nb, None)
+                             Y, FAKE, FAKE, dQ, FAKE, FAKE, dbias, FAKE, nb, None)
 
     assert bwd(bias=FAKE) == 6                      # bias without dbias
     assert bwd(dbias=FAKE) == 6
     assert bwd(dQ=ODD) == 5
     assert bwd(nb=64) == 7
     assert bwd(heads=16) == 4
+    assert bwd(bias=FAKE, dbias=FAKE, Y=None) == 1  # with a bias the row pass reads Y
+    assert b"Y is NULL" in L.gt_last_error()
+    assert bwd(bias=FAKE, dbias=FAKE, Y=ODD) == 5
 
 
 def test_work_bytes_grow_with_graph(L):

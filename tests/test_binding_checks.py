@@ -52,18 +52,20 @@ def test_fwd_rejects_wrong_outputs():
 
 def test_bwd_rejects_wrong_tensors():
     Q, K, V = _qkv()
-    lse, dY = torch.zeros(R, H), torch.zeros(R, H, DH)
+    Y, lse, dY = torch.zeros(R, H, DH), torch.zeros(R, H), torch.zeros(R, H, DH)
     g = _graph()
+    with pytest.raises(ValueError, match="Y has shape"):
+        T.gt_attn_bwd(g, Q, K, V, torch.zeros(R, H, DH - 1), lse, dY)
     with pytest.raises(ValueError, match="lse has shape"):
-        T.gt_attn_bwd(g, Q, K, V, torch.zeros(R, H + 1), dY)
+        T.gt_attn_bwd(g, Q, K, V, Y, torch.zeros(R, H + 1), dY)
     with pytest.raises(ValueError, match="dY has shape"):
-        T.gt_attn_bwd(g, Q, K, V, lse, torch.zeros(R - 1, H, DH))
+        T.gt_attn_bwd(g, Q, K, V, Y, lse, torch.zeros(R - 1, H, DH))
     with pytest.raises(ValueError, match="dK has shape"):
-        T.gt_attn_bwd(g, Q, K, V, lse, dY, dK=torch.zeros(R, H, DH))
+        T.gt_attn_bwd(g, Q, K, V, Y, lse, dY, dK=torch.zeros(R, H, DH))
     with pytest.raises(ValueError, match="bias and dbias"):
-        T.gt_attn_bwd(g, Q, K, V, lse, dY, dbias=torch.zeros(E, H))
+        T.gt_attn_bwd(g, Q, K, V, Y, lse, dY, dbias=torch.zeros(E, H))
     with pytest.raises(ValueError, match="dbias has shape"):
-        T.gt_attn_bwd(g, Q, K, V, lse, dY, bias=torch.zeros(E, H), dbias=torch.zeros(E, H + 1))
+        T.gt_attn_bwd(g, Q, K, V, Y, lse, dY, bias=torch.zeros(E, H), dbias=torch.zeros(E, H + 1))
 
 
 def test_host_tensors_are_refused():
@@ -72,7 +74,8 @@ def test_host_tensors_are_refused():
     with pytest.raises(ValueError, match="must be on a GPU"):
         T.gt_attn_fwd(_graph(), Q, K, V)
     with pytest.raises(ValueError, match="must be on a GPU"):
-        T.gt_attn_bwd(_graph(), Q, K, V, torch.zeros(R, H), torch.zeros(R, H, DH))
+        T.gt_attn_bwd(_graph(), Q, K, V, torch.zeros(R, H, DH), torch.zeros(R, H),
+                      torch.zeros(R, H, DH))
     with pytest.raises(ValueError, match="must be on a GPU"):
         T.gt_proj_qkv(torch.zeros(4, 64), *(torch.zeros(64, 64) for _ in range(3)))
     with pytest.raises(ValueError, match="must be on a GPU"):

@@ -37,7 +37,7 @@ def test_attention_graph_replays_match_eager(dtype):
 
     def step():
         T.gt_attn_fwd(g, Q, K, V, bias, P.scale, work, Y, lse)
-        T.gt_attn_bwd(g, Q, K, V, lse, dY, bias, P.scale, work, dQ, dK, dV, dB)
+        T.gt_attn_bwd(g, Q, K, V, Y, lse, dY, bias, P.scale, work, dQ, dK, dV, dB)
 
     step()
     torch.cuda.synchronize()

@@ -142,7 +142,7 @@ def attention_case(n, deg, H, dh, seed, thresholds=None, device="cuda"):
     print("  prepared; checking the transpose", flush=True)
     check_transpose(g, indices, o, n, deg)
     Y, lse = T.gt_attn_fwd(g, Q, K, V, bias, scale)
-    dQ, dK, dV, dB = T.gt_attn_bwd(g, Q, K, V, lse, dY, bias, scale)
+    dQ, dK, dV, dB = T.gt_attn_bwd(g, Q, K, V, Y, lse, dY, bias, scale)
     torch.cuda.synchronize()
     print("  ran fwd + bwd; comparing", flush=True)
     rt = RTOL["bf16"]

@@ -26,7 +26,7 @@ def run_gpu(P, th=None):
     d = device_problem(P)
     g = T.gt_graph_prepare(d["indptr"], d["indices"], P.cfg.n_cols, *(th or ()))
     Y, lse = T.gt_attn_fwd(g, d["Q"], d["K"], d["V"], d["bias"], P.scale)
-    dQ, dK, dV, dB = T.gt_attn_bwd(g, d["Q"], d["K"], d["V"], lse, d["dY"], d["bias"], P.scale)
+    dQ, dK, dV, dB = T.gt_attn_bwd(g, d["Q"], d["K"], d["V"], Y, lse, d["dY"], d["bias"], P.scale)
     torch.cuda.synchronize()
     return Y, lse, dQ, dK, dV, dB
 
@@ -95,12 +95,48 @@ def test_scale_other_than_default():
     d = device_problem(P)
     g = T.gt_graph_prepare(d["indptr"], d["indices"], 64, 2, 8, 8)
     Y, lse = T.gt_attn_fwd(g, d["Q"], d["K"], d["V"], d["bias"], 0.3)
-    dQ, dK, dV, dB = T.gt_attn_bwd(g, d["Q"], d["K"], d["V"], lse, d["dY"], d["bias"], 0.3)
+    dQ, dK, dV, dB = T.gt_attn_bwd(g, d["Q"], d["K"], d["V"], Y, lse, d["dY"], d["bias"], 0.3)
     rY, rl = O.fwd(ip, ix, 64, P.Q, P.K, P.V, P.bias, 0.3)
     rQ, rK, rV, rB = O.bwd(ip, ix, 64, P.Q, P.K, P.V, P.dY, P.bias, 0.3)
     for a, b, n in ((Y, rY, "Y"), (dQ, rQ, "dQ"), (dK, rK, "dK"), (dV, rV, "dV"), (dB, rB, "dB")):
         assert_close(a, b, 1e-5, n, head_axis=1 if n == "dB" else "auto")
     assert_lse(lse, rl, 1e-5)
+
+
+@pytest.mark.parametrize("dt, H, dh", [("f32", 4, 16), ("bf16", 4, 32), ("f32", 1, 64)])
+def test_minus_inf_bias_masks_edges(dt, H, dh):
+    """A -inf bias masks its edge: rows whose first edges (a whole first
+    round of a lane group, or of a wavefront's groups) are masked, rows with
+    every edge masked in one head or in all heads, and split rows whose first
+    pieces are masked, against the oracle (which treats a masked edge as
+    absent and a fully masked row as empty).  Several thresholds, so that
+    the masked edges fall in small rows, whole-wavefront rows and pieces."""
+    import dataclasses
+    rng = np.random.default_rng(81)
+    R, M = 300, 280
+    degs = _degrees(rng, R, M)
+    ip, ix = I.random_graph(81, R, M, degs, self_loops=False)
+    P = I.small_problem(81, ip, ix, M, H, dh, dt, True)
+    b = P.bias.copy()
+    deg = np.diff(ip)
+    for i in np.nonzero(deg > 0)[0]:
+        lo, d = ip[i], deg[i]
+        kind = i % 5
+        if kind == 0:      # the first few edges, every head
+            b[lo:lo + min(d, 1 + i % 9)] = -np.inf
+        elif kind == 1:    # the whole row in head 0
+            b[lo:lo + d, 0] = -np.inf
+        elif kind == 2 and i % 3 == 0:   # the whole row, every head
+            b[lo:lo + d] = -np.inf
+        elif kind == 3:    # the first half of the row (whole leading pieces of split rows)
+            b[lo:lo + d // 2, H - 1] = -np.inf
+    P = dataclasses.replace(P, bias=b)
+    for th in (None, (2, 8, 8), (0, 0, 3)):
+        print(f"minus-inf bias {dt} H={H} dh={dh} th={th}", flush=True)
+        out = run_gpu(P, th)
+        for t in out:
+            assert not torch.isnan(t).any()
+        check_full(P, out)
 
 
 def test_bitwise_determinism():
@@ -130,7 +166,7 @@ def test_one_graph_two_concurrent_streams():
 
     def step(d, P):
         Y, lse = T.gt_attn_fwd(g, d["Q"], d["K"], d["V"], d["bias"], P.scale)
-        return (Y, lse) + T.gt_attn_bwd(g, d["Q"], d["K"], d["V"], lse, d["dY"], d["bias"], P.scale)
+        return (Y, lse) + T.gt_attn_bwd(g, d["Q"], d["K"], d["V"], Y, lse, d["dY"], d["bias"], P.scale)
 
     alone = [step(d, P) for d, P in zip(devs, probs)]
     torch.cuda.synchronize()
