@@ -172,6 +172,59 @@ extern "C" gt_status gt_attn_fwd(const gt_graph *g, int32_t heads, int32_t head_
                     (float *)(wb + w.part_fwd), (hipStream_t)stream);
 }
 
+// ---- forward without a caller workspace ------------------------------------
+// The piece states of split rows live in a file-scope device array instead
+// of the caller's work buffer.  Host code never uses the array's name as an
+// address: on the first call on a device (with that device current) its
+// device address is looked up with hipGetSymbolAddress and kept per device.
+static __device__ __align__(256) unsigned char scratch[GT_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+std::mutex g_scratch_mu;
+std::vector<void *> g_scratch_at;   // device address of `scratch`, per device id
+
+gt_status scratch_address(void **out) {
+  int dev = 0;
+  GT_HIP(hipGetDevice(&dev));
+  std::lock_guard<std::mutex> lk(g_scratch_mu);
+  if ((size_t)dev >= g_scratch_at.size()) g_scratch_at.resize((size_t)dev + 1, nullptr);
+  if (!g_scratch_at[dev]) {
+    void *p = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !p)
+      return fail(GT_E_HIP, "hipGetSymbolAddress(scratch) on device %d: %s", dev,
+                  hipGetErrorString(e));
+    g_scratch_at[dev] = p;
+  }
+  *out = g_scratch_at[dev];
+  return GT_OK;
+}
+}  // namespace
+
+extern "C" gt_status gt_attn_fwd_noalloc(const gt_graph *g, int32_t heads, int32_t head_dim,
+                                         gt_dtype dt, float scale, const void *Q, const void *K,
+                                         const void *V, const float *bias, void *Y, float *lse,
+                                         void *stream) {
+  clear_error();
+  TRY(check_common(g, heads, head_dim, dt));
+  const bool rows = g->n_rows > 0, cols = g->n_cols > 0;
+  TRY(check_feat(Q, "Q", rows));
+  TRY(check_feat(K, "K", cols));
+  TRY(check_feat(V, "V", cols));
+  TRY(check_feat(Y, "Y", rows));
+  if (rows && !lse) return fail(GT_E_NULL, "lse is NULL");
+  if (lse && !aligned4(lse)) return fail(GT_E_ALIGN, "lse is not 4-byte aligned");
+  if (bias && !aligned4(bias)) return fail(GT_E_ALIGN, "bias is not 4-byte aligned");
+  const WorkLayout w = work_layout(g, heads, head_dim);
+  if (w.fwd_total > (size_t)GT_NOALLOC_SCRATCH_BYTES)
+    return fail(GT_E_WORKSPACE, "the forward needs %zu bytes of scratch; the static maximum is %zu",
+                w.fwd_total, (size_t)GT_NOALLOC_SCRATCH_BYTES);
+  void *ptr = nullptr;
+  TRY(scratch_address(&ptr));
+  return launch_fwd(g, heads, head_dim, dt, scale, Q, K, V, bias, Y, lse,
+                    (float *)((char *)ptr + w.part_fwd), (hipStream_t)stream);
+}
+
 extern "C" gt_status gt_attn_bwd(const gt_graph *g, int32_t heads, int32_t head_dim, gt_dtype dt,
                                  float scale, const void *Q, const void *K, const void *V,
                                  const float *bias, const void *Y, const float *lse,
@@ -262,4 +315,4 @@ extern "C" const char *gt_status_str(gt_status s) {
 
 extern "C" const char *gt_last_error(void) { return g_err; }
 
-extern "C" int32_t gt_version(void) { return 102; }
+extern "C" int32_t gt_version(void) { return 103; }

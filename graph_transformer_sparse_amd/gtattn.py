@@ -82,6 +82,7 @@ def lib():
         "gt_csr_validate": (_i32, [_P, _P, _i64, _i64, _i64, _P, _sz, C.POINTER(_i32), _P]),
         "gt_attn_work_bytes": (_sz, [G, _i32, _i32]),
         "gt_attn_fwd": (_i32, [G, _i32, _i32, _i32, _f32, _P, _P, _P, _P, _P, _P, _P, _sz, _P]),
+        "gt_attn_fwd_noalloc": (_i32, [G, _i32, _i32, _i32, _f32, _P, _P, _P, _P, _P, _P, _P]),
         "gt_attn_bwd": (_i32, [G, _i32, _i32, _i32, _f32, _P, _P, _P, _P, _P, _P, _P,
                                _P, _P, _P, _P, _P, _sz, _P]),
         "gt_prof_enable": (_i32, [_i32]),
@@ -312,6 +313,22 @@ def gt_attn_fwd(g: Graph, Q, K, V, bias=None, scale=None, work=None, Y=None, lse
     _check(lib().gt_attn_fwd(C.byref(g.st), H, dh, _dt(Q.dtype), scale, _ptr(Q), _ptr(K),
                              _ptr(V), _ptr(bias), _ptr(Y), _ptr(lse), _ptr(work),
                              work.numel(), _stream(Q.device)), "gt_attn_fwd")
+    return Y, lse
+
+
+def gt_attn_fwd_noalloc(g: Graph, Q, K, V, bias=None, scale=None, Y=None, lse=None):
+    """Forward with the library's static scratch (no workspace argument):
+    returns (Y, lse).  Allocates Y and lse only if they are not given."""
+    R, H, dh, dt, dev = _attn_shapes("gt_attn_fwd_noalloc", g, Q, K, V, bias)
+    scale = dh ** -0.5 if scale is None else float(scale)
+    Y = torch.empty_like(Q) if Y is None else Y
+    lse = torch.empty((R, H), dtype=torch.float32, device=dev) if lse is None else lse
+    _tensor("gt_attn_fwd_noalloc", "Y", Y, (R, H, dh), dt, dev)
+    _tensor("gt_attn_fwd_noalloc", "lse", lse, (R, H), torch.float32, dev)
+    _on_gpu("gt_attn_fwd_noalloc", g, dev)
+    _check(lib().gt_attn_fwd_noalloc(C.byref(g.st), H, dh, _dt(Q.dtype), scale, _ptr(Q), _ptr(K),
+                                     _ptr(V), _ptr(bias), _ptr(Y), _ptr(lse), _stream(Q.device)),
+           "gt_attn_fwd_noalloc")
     return Y, lse
 
 

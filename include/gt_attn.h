@@ -185,6 +185,26 @@ gt_status gt_attn_fwd(const gt_graph *g, int32_t heads, int32_t head_dim, gt_dty
                       const float *bias, void *Y, float *lse, void *work, size_t work_bytes,
                       void *stream);
 
+/* The forward for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc): gt_attn_fwd without the `work` argument.  Its scratch (the
+ * softmax states of split rows) is a static device array of
+ * GT_NOALLOC_SCRATCH_BYTES, one per GPU, held until the process ends; the
+ * call allocates nothing.  Same arguments, results (bitwise) and errors as
+ * gt_attn_fwd, plus GT_E_WORKSPACE when the graph needs more scratch than
+ * that (gt_attn_work_bytes bounds it; a graph's split rows need about
+ * 4 (heads * head_dim + 2 heads) bytes per `chunk` nonzeros of its rows
+ * longer than t_mid) and GT_E_HIP if the array's address cannot be found.
+ * The first call on a device looks that address up.  Nothing in the array
+ * needs clearing: every state is written before it is read.  Every call on a
+ * GPU shares that GPU's array: calls that overlap on one GPU (several
+ * streams, or several host threads) race and must be serialised by the
+ * caller. */
+#define GT_NOALLOC_SCRATCH_BYTES (16u << 20)
+gt_status gt_attn_fwd_noalloc(const gt_graph *g, int32_t heads, int32_t head_dim, gt_dtype dt,
+                              float scale, const void *Q, const void *K, const void *V,
+                              const float *bias, void *Y, float *lse, void *stream);
+
 /* Backward (Section 2.2): given Y and lse of gt_attn_fwd and the output
  * gradient dY [n_rows, heads, head_dim], writes dQ [n_rows, heads,
  * head_dim], dK, dV [n_cols, heads, head_dim] (all dt, every element
@@ -224,7 +244,7 @@ gt_status gt_prof_query(const char *kernel, double *total_ms, int64_t *launches)
 const char *gt_status_str(gt_status s);
 /* Detail of the last failed call on this thread ("" if none). */
 const char *gt_last_error(void);
-/* Version of the ABI: 102 (gt_attn_bwd takes the forward's Y). */
+/* Version of the ABI: 103 (gt_attn_fwd_noalloc; gt_attn_bwd takes the forward's Y). */
 int32_t gt_version(void);
 
 #ifdef __cplusplus

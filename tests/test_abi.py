@@ -92,6 +92,24 @@ def test_fwd_argument_checks(L):
     assert _fwd(L, ung) == 1                        # not prepared
 
 
+def test_fwd_noalloc_argument_checks(L):
+    """The static-scratch forward checks its arguments like gt_attn_fwd and
+    refuses, before touching the device, a graph whose split rows need more
+    scratch than its static array holds."""
+    def call(g, Q=FAKE, Y=FAKE, lse=FAKE, dh=32):
+        return L.gt_attn_fwd_noalloc(C.byref(g) if g is not None else None, 4, dh, T.GT_F32, 0.1,
+                                     Q, FAKE, FAKE, None, Y, lse, None)
+    g = _fake_graph()
+    assert call(None) == 1
+    assert call(g, dh=48) == 4
+    assert call(g, Q=ODD) == 5
+    assert call(g, lse=None) == 1
+    # 4 heads x 32: (128 + 8) floats per piece state, so 31,000 pieces need 16.9 MB
+    big = _fake_graph(n_items=31_000)
+    assert call(big) == 7
+    assert b"static maximum" in L.gt_last_error()
+
+
 def test_bwd_argument_checks(L):
     g = _fake_graph()
 
