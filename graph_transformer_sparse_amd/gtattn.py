@@ -228,24 +228,20 @@ class Graph:
 
 def gt_graph_prepare(indptr: torch.Tensor, indices: torch.Tensor, n_cols: int,
                      t_small: int | None = None, t_mid: int | None = None,
-                     chunk: int | None = None, validate: bool | None = None) -> Graph:
-    """Prepare a device CSR (int32 indptr/indices) for attention.  With
-    validate (default: the environment variable GT_DEBUG=1) the CSR content
-    is checked on the GPU first (gt_csr_validate) and a malformed graph
-    raises instead of giving undefined results."""
+                     chunk: int | None = None, validate: bool = True) -> Graph:
+    """Prepare a device CSR (int32 indptr/indices) for attention.  The CSR
+    content is checked on the GPU first (gt_csr_validate: row pointer
+    monotone and consistent, every column in [0, n_cols), columns strictly
+    ascending in each row), and a malformed graph raises GTError instead of
+    reaching the kernels, whose gathers trust the column indices.  A caller
+    that has already checked the graph may pass validate=False."""
     L = lib()
-    if validate is None:
-        validate = os.environ.get("GT_DEBUG", "0") == "1"
     # tuning overrides of the schedule's defaults (GT_TIER_SMALL, GT_TIER_MID,
     # GT_TIER_CHUNK); explicit arguments win
     env = lambda k: int(os.environ[k]) if os.environ.get(k) else None
     t_small = env("GT_TIER_SMALL") if t_small is None else t_small
     t_mid = env("GT_TIER_MID") if t_mid is None else t_mid
     chunk = env("GT_TIER_CHUNK") if chunk is None else chunk
-    if validate:
-        code = gt_csr_validate(indptr, indices, n_cols)
-        if code != 0:
-            raise GTError(8, "gt_graph_prepare", f"malformed CSR (gt_csr_validate code {code})")
     d_small, d_mid, d_chunk = gt_graph_thresholds(indices.numel())
     t_small = d_small if t_small is None else t_small
     t_mid = d_mid if t_mid is None else t_mid
@@ -259,6 +255,10 @@ def gt_graph_prepare(indptr: torch.Tensor, indices: torch.Tensor, n_cols: int,
     _need(indptr.device.type == "cuda" and indices.device == indptr.device, where,
           "indptr and indices must be on the same GPU")
     R, E = indptr.numel() - 1, indices.numel()
+    if validate:
+        code = gt_csr_validate(indptr, indices, n_cols)
+        if code != 0:
+            raise GTError(8, "gt_graph_prepare", f"malformed CSR (gt_csr_validate code {code})")
     nb = L.gt_graph_meta_bytes(R, n_cols, E, chunk)
     if nb == 0:
         raise GTError(2, "gt_graph_meta_bytes", "sizes out of range")

@@ -119,13 +119,13 @@ def test_validator_codes():
     assert T.gt_csr_validate(dev(big_ip), dev(big_ix), 2000) == 0
 
 
-def test_prepare_validates_on_request():
-    """validate=True (or GT_DEBUG=1) checks the CSR before any prep kernel
+def test_prepare_validates_by_default():
+    """The binding's prepare checks the CSR (unless validate=False) before any prep kernel
     runs and raises on a malformed graph; a valid one prepares as usual."""
     ip, ix = I.csr_from_rows([[0, 2], [1], [], [0, 1, 3]], 4)
     bad = np.array([0, 2, 1, 0, 1, 4], np.int32)           # a column out of range
     with pytest.raises(T.GTError):
-        T.gt_graph_prepare(dev(ip), dev(bad), 4, validate=True)
+        T.gt_graph_prepare(dev(ip), dev(bad), 4)
     g = T.gt_graph_prepare(dev(ip), dev(ix), 4, validate=True)
     assert g.nnz == ix.size
 

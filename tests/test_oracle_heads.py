@@ -1,7 +1,8 @@
 """Pins of the head-repack oracle (oracle/heads.py) against the exchange it
-stands for (the paper's Section 3.2 / Algorithm 2 and the blog page's GP-A2A
-notes, simulated among p workers), brute force on small arrays, and the
-property GP-A2A rests on: attention heads are computed independently."""
+stands for (the paper's Section 3.2 / Algorithm 2, as an index map over p
+workers' blocks, with blocks of unequal size), brute force on small arrays,
+and the property GP-A2A rests on: attention heads are computed
+independently."""
 import numpy as np
 import pytest
 
@@ -41,6 +42,23 @@ def test_split_equals_the_exchange(parts):
     for k in range(parts):
         assert np.array_equal(back[k], blocks[k])
     assert np.array_equal(np.concatenate(back, axis=0), Hd.head_merge(s))
+
+
+def test_exchange_with_unequal_blocks():
+    """Workers holding different numbers of nodes (one holding none): the
+    head-partitioned tensors are still head_split of the concatenated nodes,
+    and the reverse exchange gives every worker its own block back."""
+    counts = [3, 0, 5, 2]
+    x = _x(sum(counts), 8, 2, seed=9)
+    starts = np.concatenate([[0], np.cumsum(counts)])
+    blocks = [x[starts[k]:starts[k + 1]] for k in range(4)]
+    got = Hd.all_to_all_node_to_head(blocks)
+    s = Hd.head_split(x, 4)
+    for r in range(4):
+        assert np.array_equal(got[r], s[r])
+    back = Hd.all_to_all_head_to_node(got, counts)
+    for k in range(4):
+        assert np.array_equal(back[k], blocks[k])
 
 
 def test_round_trip_identity_and_per_head():
