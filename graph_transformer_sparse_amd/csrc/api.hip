@@ -315,4 +315,4 @@ extern "C" const char *gt_status_str(gt_status s) {
 
 extern "C" const char *gt_last_error(void) { return g_err; }
 
-extern "C" int32_t gt_version(void) { return 103; }
+extern "C" int32_t gt_version(void) { return 104; }

@@ -16,6 +16,8 @@
 
 #include <algorithm>
 
+#include <vector>
+
 #include "device.hpp"
 #include "host.hpp"
 #include "layout.hpp"
@@ -433,6 +435,51 @@ struct SchedJob {
   Misc m;               // host copy of the counters
 };
 
+// Piece order (the definition is in gt_attn.h): the pieces of the big
+// segments, written segment after segment, are dealt to the XCDs by their
+// position in their segment.  Workgroups go to the XCDs in turn and hold
+// four wavefronts each, so block k of the list (items 4k .. 4k + 3) runs on
+// XCD k mod 8; queue x holds the pieces in the x-th eighth of their
+// segments, in position order, so each XCD works on one eighth of every big
+// segment's range (of columns for the rows of A, of source rows for the
+// columns of A^T) at a time, and the rows those pieces gather are shared in
+// its L2.  Slots stay the segment-major indices, so the merges are
+// unchanged.  The list is short (about nnz / chunk items), so it is dealt on
+// the host, which prepare synchronises with anyway.
+static gt_status deal_items(gt_sched *out, hipStream_t s) {
+  const int64_t n = out->n_items;
+  std::vector<int32_t> it((size_t)n * 4), dealt((size_t)n * 4);
+  GT_HIP(hipMemcpyAsync(it.data(), out->items, sizeof(int32_t) * 4 * (size_t)n,
+                        hipMemcpyDeviceToHost, s));
+  GT_HIP(hipStreamSynchronize(s));
+  // bucket q of every piece, then the pieces of each bucket in list order
+  std::vector<int64_t> byq[64];
+  for (int64_t i = 0; i < n;) {
+    int64_t e = i;
+    while (e < n && it[4 * e] == it[4 * i]) ++e;   // the pieces of one segment
+    const int64_t nch = e - i;
+    for (int64_t c = 0; c < nch; ++c) byq[(64 * (2 * c + 1)) / (2 * nch)].push_back(i + c);
+    i = e;
+  }
+  std::vector<int64_t> q[8];
+  for (int b = 0; b < 64; ++b) q[b / 8].insert(q[b / 8].end(), byq[b].begin(), byq[b].end());
+  size_t head[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+  int64_t pos = 0;
+  for (int64_t k = 0; pos < n; ++k) {
+    for (int t = 0; t < 4 && pos < n; ++t) {
+      int x = (int)(k % 8);
+      while (head[x] == q[x].size()) x = (x + 1) % 8;
+      const int64_t src = q[x][head[x]++];
+      for (int f = 0; f < 4; ++f) dealt[4 * pos + f] = it[4 * src + f];
+      ++pos;
+    }
+  }
+  GT_HIP(hipMemcpyAsync(out->items, dealt.data(), sizeof(int32_t) * 4 * (size_t)n,
+                        hipMemcpyHostToDevice, s));
+  GT_HIP(hipStreamSynchronize(s));
+  return GT_OK;
+}
+
 static gt_status build_schedules(SchedJob (&jobs)[2], int32_t t_small, int32_t t_mid,
                                  int32_t chunk, const SortBufs &b, hipStream_t s) {
   const int TB = 256;
@@ -497,6 +544,10 @@ static gt_status build_schedules(SchedJob (&jobs)[2], int32_t t_small, int32_t t
     out->n_items = j.m.n_big > 0 ? j.m.n_items : 0;
     out->n_merges = j.m.n_big > 0 ? j.m.n_merges : 0;
     out->max_degree = j.m.max_degree;
+    if (out->n_items > 1) {
+      const gt_status st2 = deal_items(out, s);
+      if (st2 != GT_OK) return st2;
+    }
   }
   return GT_OK;
 }

@@ -89,12 +89,22 @@ typedef enum { GT_F32 = 0, GT_BF16 = 1 } gt_dtype;
  *   n_big    = #segments with degree >  t_mid   (they lead `order`);
  *   n_mid    = #segments with t_small < degree <= t_mid (next in `order`);
  *   n_small  = #segments with degree <= t_small (the tail of `order`);
- *   items    = [n_items][4] int32: every big segment s, in `order`, with
- *              degree d is cut into nch = ceil(d / chunk) pieces; piece c is
- *              (s, ptr[s] + floor(c d / nch), ptr[s] + floor((c+1) d / nch),
- *              slot) where slot is the item's own index if nch > 1, else -1;
- *   merges   = [n_merges][3] int32: (s, first item, nch) for every big
- *              segment with nch > 1;
+ *   pieces   = every big segment s, in `order`, with degree d is cut into
+ *              nch = ceil(d / chunk) pieces; piece c is (s, ptr[s] +
+ *              floor(c d / nch), ptr[s] + floor((c+1) d / nch), slot), where
+ *              slot is the piece's index in this segment-major enumeration
+ *              if nch > 1, else -1;
+ *   items    = [n_items][4] int32: the pieces, dealt by position: piece c of
+ *              nch gets q = floor(64 (2c + 1) / (2 nch)) and queue
+ *              x = floor(q / 8), a queue being ordered by (q, segment-major
+ *              index); block k of the list (items 4k .. 4k + 3) takes its
+ *              items from queue k mod 8 and, once that queue is empty, from
+ *              queues k + 1, k + 2, ... (mod 8) in turn.  (Workgroups of
+ *              four wavefronts go to the eight XCDs in turn, so each XCD
+ *              works on one eighth of every big segment's range at a time.)
+ *   merges   = [n_merges][3] int32: (s, first slot, nch) for every big
+ *              segment with nch > 1 (its pieces' slots are first ..
+ *              first + nch - 1);
  *   spans    = [n_seg][2] int32: (ptr[order[k]], ptr[order[k] + 1]), the
  *              extent of the k-th segment of `order` (so a kernel finds a
  *              segment's nonzeros without a second, dependent load).
@@ -244,7 +254,8 @@ gt_status gt_prof_query(const char *kernel, double *total_ms, int64_t *launches)
 const char *gt_status_str(gt_status s);
 /* Detail of the last failed call on this thread ("" if none). */
 const char *gt_last_error(void);
-/* Version of the ABI: 103 (gt_attn_fwd_noalloc; gt_attn_bwd takes the forward's Y). */
+/* Version of the ABI: 104 (pieces dealt to the XCDs; gt_attn_fwd_noalloc; gt_attn_bwd
+ * takes the forward's Y). */
 int32_t gt_version(void);
 
 #ifdef __cplusplus

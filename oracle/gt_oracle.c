@@ -97,11 +97,55 @@ void or_transpose(i64 R, i64 M, i64 E, const i32 *indptr, const i32 *indices,
  *   n_small= #segments with degree <= t_small;
  *   every big segment s (in order) with degree d is cut into
  *   nch = ceil(d / chunk) pieces, piece c covering
- *   [ptr[s] + floor(c*d/nch), ptr[s] + floor((c+1)*d/nch)); each piece is one
- *   item (s, begin, end, slot), slot = the item's own index when nch > 1 and
- *   -1 otherwise; every big segment with nch > 1 gives one merge record
- *   (s, first item, nch).
+ *   [ptr[s] + floor(c*d/nch), ptr[s] + floor((c+1)*d/nch)); each piece is
+ *   (s, begin, end, slot), slot = its index in this segment-major
+ *   enumeration when nch > 1 and -1 otherwise; every big segment with
+ *   nch > 1 gives one merge record (s, first slot, nch);
+ *   the item list is the pieces dealt by position: piece c of a segment cut
+ *   into nch gets bucket q = floor(64 (2c+1) / (2 nch)), and queue
+ *   floor(q / 8); within a queue the pieces go by bucket, then by their
+ *   segment-major index; the list is filled four items at a time, the k-th
+ *   four from queue k mod 8, or, while that queue is empty, from the next
+ *   queue (k+1, k+2, ... mod 8) that is not.
  * Returns the number of items, or -1 if cap_items / cap_merges is exceeded. */
+static void deal_by_position(i64 ni, i32 *items) {
+  i32 *pieces = (i32 *)malloc(sizeof(i32) * 4 * (size_t)(ni + 1));
+  i64 *q = (i64 *)malloc(sizeof(i64) * (size_t)(ni + 1));
+  memcpy(pieces, items, sizeof(i32) * 4 * (size_t)ni);
+  /* bucket of each piece */
+  for (i64 i = 0; i < ni;) {
+    i64 e = i;
+    while (e < ni && pieces[4 * e] == pieces[4 * i]) e++;
+    i64 nch = e - i;
+    for (i64 c = 0; c < nch; ++c) q[i + c] = (64 * (2 * c + 1)) / (2 * nch);
+    i = e;
+  }
+  /* the eight queues as index lists: each one scans the buckets of its
+   * eighth in order, and each bucket the pieces in segment-major order */
+  i64 *queue[8], qlen[8], used[8];
+  for (int x = 0; x < 8; ++x) {
+    queue[x] = (i64 *)malloc(sizeof(i64) * (size_t)(ni + 1));
+    qlen[x] = 0;
+    used[x] = 0;
+    for (i64 b = 8 * x; b < 8 * x + 8; ++b)
+      for (i64 i = 0; i < ni; ++i)
+        if (q[i] == b) queue[x][qlen[x]++] = i;
+  }
+  i64 filled = 0;
+  for (i64 k = 0; filled < ni; ++k) {
+    for (int t = 0; t < 4 && filled < ni; ++t) {
+      int x = (int)(k % 8);
+      while (used[x] == qlen[x]) x = (x + 1) % 8;
+      i64 src = queue[x][used[x]++];
+      memcpy(items + 4 * filled, pieces + 4 * src, sizeof(i32) * 4);
+      filled++;
+    }
+  }
+  for (int x = 0; x < 8; ++x) free(queue[x]);
+  free(q);
+  free(pieces);
+}
+
 static const i32 *g_sort_ptr;
 static int cmp_deg_desc(const void *a, const void *b) {
   i32 x = *(const i32 *)a, y = *(const i32 *)b;
@@ -149,6 +193,7 @@ i64 or_schedule(i64 n, const i32 *ptr, i32 t_small, i32 t_mid, i32 chunk, i32 *o
     }
   }
   *n_merges_out = nmg;
+  deal_by_position(ni, items);
   return ni;
 }
 

@@ -471,10 +471,16 @@ def test_schedule_definition(ts, tm, ch):
     np.testing.assert_array_equal(S["order"], np.argsort(-degs, kind="stable"))
     nb, nm, ns = S["counts"]
     assert nb == (degs > tm).sum() and nm == ((degs > ts) & (degs <= tm)).sum() and ns == (degs <= ts).sum()
-    items = S["items"]
+    dealt = S["items"]
+    # the segment-major enumeration of the pieces: by the order of their
+    # segment in `order`, then by position in the segment
+    rank = np.empty(degs.size, np.int64)
+    rank[S["order"]] = np.arange(degs.size)
+    items = dealt[np.lexsort((dealt[:, 1], rank[dealt[:, 0]]))] if len(dealt) else dealt
     big = S["order"][:nb]
     k = 0
     merges = []
+    pos, nchs = [], []
     for r in big:
         d = degs[r]
         nch = -(-d // ch)
@@ -490,9 +496,33 @@ def test_schedule_definition(ts, tm, ch):
             merges.append((r, k, nch))
         else:
             assert part[0, 3] == -1
+        pos += list(range(nch))
+        nchs += [nch] * nch
         k += nch
     assert k == len(items)
     np.testing.assert_array_equal(S["merges"].reshape(-1, 3), np.array(merges, np.int32).reshape(-1, 3))
+    if not len(dealt):
+        return
+    # the dealing, by its properties: piece c of nch sits at the midpoint
+    # (c + 1/2) / nch of its segment; its queue is the eighth of [0, 1) that
+    # holds the midpoint; a queue's pieces keep their order by the 64th of
+    # [0, 1) that holds the midpoint, then by the segment-major order; and
+    # as long as every queue still has pieces, the k-th four come from queue
+    # k mod 8
+    c2, n2 = 2 * np.asarray(pos) + 1, 2 * np.asarray(nchs)      # midpoint = c2 / n2
+    where = {tuple(t): i for i, t in enumerate(map(tuple, items))}
+    idx = np.array([where[tuple(t)] for t in dealt])            # segment-major index of each
+    b64 = (64 * c2[idx]) // n2[idx]
+    x = (8 * c2[idx]) // n2[idx]
+    assert np.all(x == b64 // 8)
+    for q in range(8):
+        sel = np.nonzero(x == q)[0]
+        key = b64[sel] * len(items) + idx[sel]
+        assert np.all(np.diff(key) > 0), q
+    counts = np.bincount(x, minlength=8)
+    full = 4 * 8 * int(counts.min() // 4)        # blocks dealt before any queue can run short
+    p = np.arange(full)
+    np.testing.assert_array_equal(x[:full], (p // 4) % 8)
 
 
 # ----------------------------------------------------------------------------
