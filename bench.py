@@ -246,20 +246,20 @@ def unique_bytes(cfg, R, M, E, reads_y):
     return fwd + bwd
 
 
-def counter_record(workload: str):
+def counter_record(workload: str, bias: bool):
     """Counter-measured bytes (FETCH_SIZE + WRITE_SIZE, calibrated) of one
-    step's three main kernels from the committed rocprofv3 records of this
-    workload -- a stored record, used only if every one was taken on the
-    current kernel sources (the merges, under 0.3 % of a step, have no
-    record)."""
+    step's main kernels (the three passes, and with a bias the pass that
+    finishes dbias) from the committed rocprofv3 records of this workload --
+    a stored record, used only if every one was taken on the current kernel
+    sources (the merges, under 0.3 % of a step, have no record)."""
     per = {}
-    for k in ("fwd", "bwd_rows", "bwd_cols"):
+    for k in ("fwd", "bwd_rows", "bwd_cols") + (("bwd_dbias",) if bias else ()):
         v = traffic_record(k, workload)
         if v is None:
             return None
         per[k] = v
     return {"bytes_per_step": sum(per.values()), "per_kernel": per,
-            "source": f"profiles/traffic_{{fwd,bwd_rows,bwd_cols}}_{workload}.txt",
+            "source": f"profiles/traffic_{{{','.join(per)}}}_{workload}.txt",
             "source_hash": kernel_source_hash(), "stored": True}
 
 
@@ -481,7 +481,7 @@ def run_workload(args, cfg, headline: bool):
     # the committed counter records are for each workload's own shape and size
     shaped = not (args.hidden or args.nodes)
     traffic = traffic_record(dominant, cfg.name) if shaped else None
-    counters = counter_record(cfg.name) if shaped else None
+    counters = counter_record(cfg.name, cfg.bias) if shaped else None
     total_model = sum(model.values())
     uniq = unique_bytes(cfg, R, M, E, reads_y)
     step_s = ms_step * 1e-3
