@@ -12,18 +12,16 @@ namespace gt {
 // handled by a lane group inside a wavefront; longer ones by whole
 // wavefronts, in pieces of at most DEFAULT_CHUNK nonzeros.
 constexpr int32_t DEFAULT_T_SMALL = 32;
-constexpr int32_t DEFAULT_CHUNK = 512;
+constexpr int32_t DEFAULT_CHUNK = 256;
 
-// Pieces grow with the graph: a wavefront walks a piece's nonzeros one round
-// after another, so a piece must stay short against the whole pass (on a
-// 1.8M-nonzero graph 1024-nonzero pieces cost 20 %), while on graphs of
-// 8M nonzeros and more, 2048-nonzero pieces save merge work and piece
-// starts (2-7 % on 15-62M nonzeros, measured).
-constexpr int64_t LARGE_GRAPH_NNZ = 8 << 20;
-constexpr int32_t LARGE_GRAPH_CHUNK = 2048;
-inline int32_t chunk_for(int64_t nnz) {
-  return nnz >= LARGE_GRAPH_NNZ ? LARGE_GRAPH_CHUNK : DEFAULT_CHUNK;
-}
+// Pieces are dealt to the XCDs by their position in their segment, so the
+// shorter the pieces, the narrower the range of rows each XCD gathers at a
+// time (and the more merge work).  Measured with the dealt order, per step
+// (2048 / 512 / 256-nonzero pieces): Hub 12.86 / 12.26 / 12.15 ms, Large
+// 6.63 / 6.42 / 6.35 ms, Mid (512 / 256) 0.625 / 0.623 ms.  Before the
+// dealing, pieces of 2048 were the better choice from 8M nonzeros on; now
+// one size serves every graph.
+inline int32_t chunk_for(int64_t) { return DEFAULT_CHUNK; }
 
 constexpr int SORT_TILE_ITEMS = 4096;   // items per radix-sort block
 constexpr int SCAN_TILE_ITEMS = 4096;   // items per scan block

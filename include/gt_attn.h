@@ -153,13 +153,12 @@ gt_status gt_graph_prepare(const int32_t *indptr, const int32_t *indices, int64_
                            int32_t chunk, void *meta, size_t meta_bytes, gt_graph *out,
                            void *stream);
 
-/* The thresholds the kernels are tuned for: t_small, t_mid, chunk (those of
- * graphs below 8M nonzeros). */
+/* The thresholds the kernels are tuned for: t_small = 32, t_mid = chunk = 256. */
 void gt_default_thresholds(int32_t *t_small, int32_t *t_mid, int32_t *chunk);
 
-/* The tuned thresholds for a graph of nnz nonzeros: as gt_default_thresholds,
- * except that pieces (chunk = t_mid) grow to 2048 nonzeros from 8M nonzeros
- * on, where a pass is long enough for a wavefront to walk them. */
+/* The tuned thresholds for a graph of nnz nonzeros (the same for every size
+ * since the pieces are dealt to the XCDs by position; kept so that callers
+ * need not assume that). */
 void gt_graph_thresholds(int64_t nnz, int32_t *t_small, int32_t *t_mid, int32_t *chunk);
 
 /* Debug check of CSR content (the oracle's codes): 0 valid; 1 indptr[0] != 0

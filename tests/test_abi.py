@@ -41,13 +41,10 @@ def test_status_strings(L):
 
 def test_default_thresholds(L):
     ts, tm, ch = T.gt_default_thresholds()
-    assert 0 <= ts <= tm and ch >= 1
-    # by graph size: the defaults below 8M nonzeros, longer pieces from there
-    for nnz in (0, 1000, 1_842_047, (8 << 20) - 1):
+    assert (ts, tm, ch) == (32, 256, 256)
+    # one size serves every graph (pieces are dealt to the XCDs by position)
+    for nnz in (0, 1000, 1_842_047, 8 << 20, 62_000_000, 2_147_483_000):
         assert T.gt_graph_thresholds(nnz) == (ts, tm, ch)
-    for nnz in (8 << 20, 62_000_000, 2_147_483_000):
-        a, b, c = T.gt_graph_thresholds(nnz)
-        assert a == ts and b == c == 2048
 
 
 def _fake_graph(R=100, M=80, E=500, n_items=3):
