@@ -501,6 +501,198 @@ __global__ __launch_bounds__(RR_THREADS) void k_rows_resident(RowsGemm g, int gr
 }
 
 // ---------------------------------------------------------------------------
+// One-source row GEMM without a residual for bf16 at D = 128 and 256 (the
+// Q/K/V projections): the resident kernel above with the node strips and the
+// results staged through LDS.
+//
+// In the operand layout a 16-byte load or store instruction touches 32 rows
+// x 32 bytes, i.e. 32 cache lines.  Here a wavefront loads its 32-row strip
+// as contiguous 16-byte chunks (an instruction covers 8 rows x 128 bytes, or
+// 4 rows x 256 bytes: 8 whole lines), writes them into its own LDS slice and
+// reads them back in the operand layout; the results of a pair of 32-column
+// blocks go out the same way (packed to bf16 into the slice, then 8 rows x
+// 128 bytes per store).  What LDS the resident weights leave (160 KB in all)
+// is split among the 8 wavefronts; where a slice holds less than a strip
+// (D = 256: 4 KB, a quarter of the strip's k range), the strip is staged in
+// k phases and every 32-column block's accumulator stays live across them.
+// The global data of a phase is loaded two phases ahead, into two register
+// sets used in turn.  Chunks sit in the slice XOR-swizzled by row, so the
+// operand reads (32 rows, one chunk each) and the staging writes spread over
+// the banks.  LDS operations of one wavefront complete in order; a wait on
+// the LDS counter separates a slice's writes from the reads of other lanes.
+// ---------------------------------------------------------------------------
+template <int D, int NZ> struct Staged {
+  static constexpr int RB = 2 * D;                                   // bytes per node row
+  static constexpr int WB = NZ * D * D * 2;                          // resident weights
+  static constexpr int SLICE = (160 * 1024 - WB) / RR_WAVES;         // LDS bytes per wavefront
+  static constexpr int PB = RB < SLICE / 32 ? RB : SLICE / 32;       // bytes of a row per phase
+  static constexpr int P = RB / PB;                                  // phases per strip
+  static constexpr int KS = PB / 32;                                 // MFMA k steps per phase
+  static constexpr int CPR = PB / 16;                                // chunks of a row per phase
+  static constexpr int LPP = 32 * CPR / WAVE;                        // loads per lane per phase
+  static_assert(CPR >= 8 && P * PB == RB && SLICE >= 32 * PB && 32 * PB >= 4096, "shape");
+};
+
+__device__ inline void lds_fence() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
+
+template <int D, int NZ>
+__global__ __launch_bounds__(RR_THREADS) void k_rows_staged(RowsGemm g, int groups) {
+  using T = bf16_t;
+  using M = Mma<T>;
+  using S = Staged<D, NZ>;
+  constexpr int AV = 8, RB = S::RB, P = S::P, KS = S::KS, CPR = S::CPR, LPP = S::LPP;
+  constexpr int J = D / 32, NACC = P == 1 ? 1 : NZ * J;
+  constexpr int UNITS = (D / 2) * (D / AV);
+  __shared__ __align__(16) T Ws[NZ * D * D];
+  __shared__ __align__(16) uint4 Sl[RR_WAVES][32 * CPR];
+  const int tid = threadIdx.x, lane = tid & (WAVE - 1), h = lane / 32, m32 = lane % 32;
+  const int w = __builtin_amdgcn_readfirstlane(tid / WAVE);
+  const int nsplit = NZ == 1 ? g.nout : 1;
+  const int b = blockIdx.x, xcd = b % 8, slot = b / 8;
+  const int zs = slot % nsplit, group = slot / nsplit;
+  // stage W_z: Ws[z][n][k] = W_z[k][n] (the resident kernel's layout)
+  for (int zz = 0; zz < NZ; ++zz) {
+    const T *W = (const T *)g.B[NZ == 1 ? zs : zz][0];
+    T *Wz = Ws + zz * D * D;
+    for (int u = tid; u < UNITS; u += RR_THREADS) {
+      const int ng = u % (D / AV), kp = u / (D / AV), k0 = 2 * kp;
+      const uint4 r0 = *reinterpret_cast<const uint4 *>(W + (int64_t)k0 * D + ng * AV);
+      const uint4 r1 = *reinterpret_cast<const uint4 *>(W + (int64_t)(k0 + 1) * D + ng * AV);
+      int off[AV];
+#pragma unroll
+      for (int c = 0; c < AV; ++c) {
+        const int nn = ng * AV + c;
+        off[c] = nn * D + (((k0 / AV) ^ rsw(nn)) * AV) + k0 % AV;
+      }
+      store_pair_t<T>(Wz, r0, r1, off);
+    }
+  }
+  __syncthreads();
+  uint4 *sl = Sl[w];
+  const int64_t strips = (g.n + 31) / 32;
+  const int64_t stride = (int64_t)8 * groups * RR_WAVES;
+  const int64_t q0 = ((int64_t)group * 8 + xcd) * RR_WAVES + w;
+  const T *A = (const T *)g.A[0];
+  int woff[4];                                     // lane's weight chunks
+#pragma unroll
+  for (int c4 = 0; c4 < 4; ++c4) woff[c4] = m32 * D + (((2 * c4 + h) ^ rsw(m32)) * AV);
+
+  // phase t of this wavefront: strip q0 + (t / P) stride, k phase t % P
+  auto load_phase = [&](uint4 (&dst)[LPP], int64_t t) {
+    const int64_t q = q0 + (t / P) * stride;
+    const int p = (int)(t % P);
+    const auto ra = strip_rsrc(A, 32 * q, g.n, RB);   // rows past n (or past the strips) read 0
+#pragma unroll
+    for (int i = 0; i < LPP; ++i) {
+      const int u = i * WAVE + lane, r = u / CPR, c = u % CPR;
+      dst[i] = __builtin_bit_cast(
+          uint4, __builtin_amdgcn_raw_buffer_load_b128(ra, r * RB + p * S::PB + c * 16, 0, 0));
+    }
+  };
+  auto put_phase = [&](const uint4 (&src)[LPP]) {
+#pragma unroll
+    for (int i = 0; i < LPP; ++i) {
+      const int u = i * WAVE + lane, r = u / CPR, c = u % CPR;
+      sl[r * CPR + (c ^ (r & 7))] = src[i];
+    }
+  };
+  // the bf16 results of the block pair (j0, j0 + 1) of output z for strip q
+  auto out_pair = [&](int64_t q, int z, int j0, const v16f &a0, const v16f &a1) {
+    uint2 *s2 = reinterpret_cast<uint2 *>(sl);
+#pragma unroll
+    for (int bj = 0; bj < 2; ++bj) {
+      const v16f &a = bj ? a1 : a0;
+#pragma unroll
+      for (int gq = 0; gq < 4; ++gq) {
+        const int ch = 4 * bj + gq;              // 16-byte chunk of the 128-byte row
+        s2[2 * (m32 * 8 + (ch ^ (m32 & 7))) + h] =
+            make_uint2(bf16_rne(a[4 * gq]) | (bf16_rne(a[4 * gq + 1]) << 16),
+                       bf16_rne(a[4 * gq + 2]) | (bf16_rne(a[4 * gq + 3]) << 16));
+      }
+    }
+    lds_fence();
+    const auto rc = strip_rsrc(g.C[z], 32 * q, g.n, RB);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int u = i * WAVE + lane, r = u / 8, c = u % 8;
+      const uint4 v = sl[r * 8 + (c ^ (r & 7))];
+      __builtin_amdgcn_raw_buffer_store_b128(
+          __builtin_bit_cast(decltype(__builtin_amdgcn_raw_buffer_load_b128(rc, 0, 0, 0)), v), rc,
+          r * RB + j0 * 64 + c * 16, 0, 0);
+    }
+    lds_fence();
+  };
+  v16f acc[NACC];
+#pragma unroll
+  for (int k = 0; k < NACC; ++k)
+#pragma unroll
+    for (int v = 0; v < 16; ++v) acc[k][v] = 0.f;
+  // one phase: stage it, start the loads two phases ahead, multiply
+  auto phase = [&](int64_t t, uint4 (&cur)[LPP]) {
+    const int64_t q = q0 + (t / P) * stride;
+    const int p = (int)(t % P);
+    put_phase(cur);
+    load_phase(cur, t + 2);
+    lds_fence();
+    uint4 bv[KS];
+#pragma unroll
+    for (int c = 0; c < KS; ++c) bv[c] = sl[m32 * CPR + ((2 * c + h) ^ (m32 & 7))];
+    lds_fence();
+    if constexpr (P == 1) {
+#pragma unroll
+      for (int zz = 0; zz < NZ; ++zz) {
+        v16f held;
+#pragma unroll
+        for (int j = 0; j < J; ++j) {
+          asm volatile("" ::: "memory");
+          v16f a;
+#pragma unroll
+          for (int v = 0; v < 16; ++v) a[v] = 0.f;
+          const T *wrow = Ws + (zz * D + 32 * j) * D;
+#pragma unroll
+          for (int c = 0; c < KS; ++c) {
+            if (c % 8 == 0 && c > 0) asm volatile("" ::: "memory");
+            const uint4 wv = *reinterpret_cast<const uint4 *>(wrow + woff[c % 4] + (c / 4) * 8 * AV);
+            a = M::mma(wv, bv[c], a);
+          }
+          if (j % 2 == 0) held = a;
+          else out_pair(q, NZ == 1 ? zs : zz, j - 1, held, a);
+        }
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < J; ++j) {
+        asm volatile("" ::: "memory");
+        const T *wrow = Ws + (32 * j) * D;
+#pragma unroll
+        for (int c = 0; c < KS; ++c) {
+          const int kc = p * KS + c;               // k step within the row
+          const uint4 wv = *reinterpret_cast<const uint4 *>(wrow + woff[kc % 4] + (kc / 4) * 8 * AV);
+          acc[j] = M::mma(wv, bv[c], acc[j]);
+        }
+      }
+      if (p == P - 1) {
+#pragma unroll
+        for (int j = 0; j < J; j += 2) {
+          out_pair(q, zs, j, acc[j], acc[j + 1]);
+#pragma unroll
+          for (int v = 0; v < 16; ++v) acc[j][v] = acc[j + 1][v] = 0.f;
+        }
+      }
+    }
+  };
+  uint4 g0[LPP], g1[LPP];
+  load_phase(g0, 0);
+  load_phase(g1, 1);
+  const int64_t nt = q0 < strips ? ((strips - 1 - q0) / stride + 1) * P : 0;   // phases to run
+  for (int64_t t = 0; t < nt; t += 2) {
+    phase(t, g0);
+    if (t + 1 >= nt) break;
+    phase(t + 1, g1);
+  }
+}
+
+// ---------------------------------------------------------------------------
 // four-source row GEMM (the input gradient): C = sum_s A_s W_s^T (all but
 // fp32 at D = 256).
 //
@@ -892,12 +1084,28 @@ static void launch_resident_k(const RowsGemm &g, hipStream_t st) {
   k_rows_resident<T, D, RESID, NZ><<<grid, RR_THREADS, 0, st>>>(g, (int)groups);
 }
 
+template <int D, int NZ>
+static void launch_staged_k(const RowsGemm &g, hipStream_t st) {
+  static const int per_cu = blocks_per_cu(k_rows_staged<D, NZ>, RR_THREADS);
+  const int nsplit = NZ == 1 ? g.nout : 1;
+  const int64_t strips = cdiv(g.n, 32);
+  const int64_t cus_per_xcd = std::max(1, device_cus() / 8);
+  int64_t groups = std::max<int64_t>(1, (int64_t)per_cu * cus_per_xcd / nsplit);
+  groups = std::max<int64_t>(1, std::min<int64_t>(groups, cdiv(strips, 8 * RR_WAVES)));
+  const dim3 grid((unsigned)(8 * groups * nsplit));
+  k_rows_staged<D, NZ><<<grid, RR_THREADS, 0, st>>>(g, (int)groups);
+}
+
 // all three Q/K/V weights stay in LDS together where they fit (128 KB), so
-// each strip of X is read once; otherwise workgroups split the outputs
+// each strip of X is read once; otherwise workgroups split the outputs.
+// bf16 at D = 128 and 256 without a residual stages its strips through LDS.
 template <typename T, int D>
 static void launch_resident(const RowsGemm &g, hipStream_t st) {
   constexpr bool three_fit = 3 * D * D * (int)sizeof(T) <= 128 * 1024;
+  constexpr bool staged = sizeof(T) == 2 && (D == 128 || D == 256);
   if (g.R) launch_resident_k<T, D, true, 1>(g, st);
+  else if (staged && g.nout == 3 && three_fit) launch_staged_k<D, three_fit ? 3 : 1>(g, st);
+  else if (staged) launch_staged_k<D, 1>(g, st);
   else if (g.nout == 3 && three_fit) launch_resident_k<T, D, false, three_fit ? 3 : 1>(g, st);
   else launch_resident_k<T, D, false, 1>(g, st);
 }
