@@ -370,6 +370,11 @@ def summary(r):
                          "frac": line["roofline"]["frac"]},
             "kernels_ms": {k: v["ms_per_launch"] for k, v in d["kernels"].items()},
             "parity": par["verdict"] if par else None,
+            # the oracle's own rate in the parity check: fwd + bwd of the
+            # whole graph in float64, all host cores, with the magnitudes of
+            # its sums (the headline's cpu_baseline times it without them)
+            "oracle_GEdges_per_s": (line["config"]["nnz"] / par["oracle_s"] / 1e9
+                                    if par and par.get("oracle_s") else None),
             "parity_detail": par}
 
 
