@@ -874,7 +874,9 @@ def head_split_bench(args, cfg):
         "roofline": {"bound": "hbm", "kernel": "head_split", "achieved": ach,
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": ach / HBM_PEAK_GBS,
                      "traffic": None},
-        "cpu_baseline": None,
+        # the attention on head slices is the same mathematics as on all
+        # heads at once: the oracle's fwd + bwd of the workload stands beside it
+        "cpu_baseline": cpu_baseline(P, args.cpu_budget) if args.cpu_budget > 0 else None,
         "detail": {"head_split_ms": split_ms, "head_merge_ms": merge_ms,
                    "head_merge_GBps": nbytes / (merge_ms * 1e-3) / 1e9,
                    "bytes_per_repack": nbytes},
