@@ -693,6 +693,206 @@ __global__ __launch_bounds__(RR_THREADS) void k_rows_staged(RowsGemm g, int grou
 }
 
 // ---------------------------------------------------------------------------
+// The output projection Z = X W_o + Y for bf16 at D = 128 and 256, staged
+// like k_rows_staged.  The residual must be added to the float32 products
+// before the one rounding to bf16, so the results of a pair of 32-column
+// blocks go into the wavefront's slice as float32 (8 KB), come back as
+// contiguous runs of a row (an instruction covers 4 rows x 64 columns), have
+// the residual added (read the same contiguous way, ahead of time) and leave
+// as bf16, 4 whole lines per store.  At D = 256 a workgroup holds one half
+// of W_o's columns (NH = 2: 64 KB), so that the slices have room for the
+// float32 pair; the two workgroups of a strip sit eight indices apart (same
+// XCD), so the strip's second read of X comes from L2.
+// ---------------------------------------------------------------------------
+template <int D, int NH> struct StagedOut {
+  static constexpr int RB = 2 * D;
+  static constexpr int DC = D / NH;                                   // output columns held
+  static constexpr int WB = DC * D * 2;
+  static constexpr int SLICE = (160 * 1024 - WB) / RR_WAVES;
+  static constexpr int PB = 32 * RB <= SLICE ? RB : RB / 2;           // bytes of a row per phase
+  static constexpr int P = RB / PB;
+  static constexpr int KS = PB / 32;
+  static constexpr int CPR = PB / 16;
+  static constexpr int LPP = 32 * CPR / WAVE;
+  static constexpr int J = DC / 32;
+  static_assert(SLICE >= 32 * PB && SLICE >= 8192 && J % 2 == 0 && CPR >= 8, "shape");
+};
+
+template <int D, int NH>
+__global__ __launch_bounds__(RR_THREADS) void k_rows_staged_out(RowsGemm g, int groups) {
+  using T = bf16_t;
+  using M = Mma<T>;
+  using S = StagedOut<D, NH>;
+  constexpr int AV = 8, RB = S::RB, P = S::P, KS = S::KS, CPR = S::CPR, LPP = S::LPP;
+  constexpr int J = S::J, DC = S::DC, NACC = P == 1 ? 1 : J;
+  __shared__ __align__(16) T Ws[DC * D];
+  __shared__ __align__(16) uint4 Sl[RR_WAVES][S::SLICE / 16];
+  const int tid = threadIdx.x, lane = tid & (WAVE - 1), h = lane / 32, m32 = lane % 32;
+  const int w = __builtin_amdgcn_readfirstlane(tid / WAVE);
+  const int b = blockIdx.x, xcd = b % 8, slot = b / 8;
+  const int half = slot % NH, group = slot / NH;
+  // stage W_o's columns [half DC, half DC + DC): Ws[n][k] = W_o[k][half DC + n]
+  {
+    const T *W = (const T *)g.B[0][0];
+    constexpr int UNITS = (D / 2) * (DC / AV);
+    for (int u = tid; u < UNITS; u += RR_THREADS) {
+      const int ng = u % (DC / AV), kp = u / (DC / AV), k0 = 2 * kp;
+      const int col = half * DC + ng * AV;
+      const uint4 r0 = *reinterpret_cast<const uint4 *>(W + (int64_t)k0 * D + col);
+      const uint4 r1 = *reinterpret_cast<const uint4 *>(W + (int64_t)(k0 + 1) * D + col);
+      int off[AV];
+#pragma unroll
+      for (int c = 0; c < AV; ++c) {
+        const int nn = ng * AV + c;
+        off[c] = nn * D + (((k0 / AV) ^ rsw(nn)) * AV) + k0 % AV;
+      }
+      store_pair_t<T>(Ws, r0, r1, off);
+    }
+  }
+  __syncthreads();
+  uint4 *sl = Sl[w];
+  const int64_t strips = (g.n + 31) / 32;
+  const int64_t stride = (int64_t)8 * groups * RR_WAVES;
+  const int64_t q0 = ((int64_t)group * 8 + xcd) * RR_WAVES + w;
+  const T *A = (const T *)g.A[0];
+  int woff[4];
+#pragma unroll
+  for (int c4 = 0; c4 < 4; ++c4) woff[c4] = m32 * D + (((2 * c4 + h) ^ rsw(m32)) * AV);
+
+  auto load_phase = [&](uint4 (&dst)[LPP], int64_t t) {
+    const int64_t q = q0 + (t / P) * stride;
+    const int p = (int)(t % P);
+    const auto ra = strip_rsrc(A, 32 * q, g.n, RB);
+#pragma unroll
+    for (int i = 0; i < LPP; ++i) {
+      const int u = i * WAVE + lane, r = u / CPR, c = u % CPR;
+      dst[i] = __builtin_bit_cast(
+          uint4, __builtin_amdgcn_raw_buffer_load_b128(ra, r * RB + p * S::PB + c * 16, 0, 0));
+    }
+  };
+  auto put_phase = [&](const uint4 (&src)[LPP]) {
+#pragma unroll
+    for (int i = 0; i < LPP; ++i) {
+      const int u = i * WAVE + lane, r = u / CPR, c = u % CPR;
+      sl[r * CPR + (c ^ (r & 7))] = src[i];
+    }
+  };
+  // residual of the pair of blocks (jp, jp + 1) (local indices), in the
+  // read-back layout: run i of a lane is row (i 64 + lane) / 16, columns
+  // 4 ((i 64 + lane) % 16) .. + 3 of the pair
+  uint2 rres[J / 2][8];
+  auto load_resid = [&](int64_t q, int pr) {
+    const auto rr = strip_rsrc(g.R, 32 * q, g.n, RB);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int u = i * WAVE + lane, r = u / 16, c = u % 16;
+      rres[pr][i] = __builtin_bit_cast(
+          uint2, __builtin_amdgcn_raw_buffer_load_b64(rr, r * RB + (half * DC + 64 * pr + 4 * c) * 2, 0, 0));
+    }
+  };
+  // Z of the block pair pr: the float32 products through the slice (row m32,
+  // 16 chunks of four floats), the residual added, bf16 out
+  auto out_pair = [&](int64_t q, int pr, const v16f &a0, const v16f &a1) {
+    float4 *s4 = reinterpret_cast<float4 *>(sl);
+#pragma unroll
+    for (int bj = 0; bj < 2; ++bj) {
+      const v16f &a = bj ? a1 : a0;
+#pragma unroll
+      for (int gq = 0; gq < 4; ++gq) {
+        const int ch = 8 * bj + 2 * gq + h;     // four columns 32 bj + 8 gq + 4 h ..
+        s4[m32 * 16 + (ch ^ (m32 & 7))] = make_float4(a[4 * gq], a[4 * gq + 1], a[4 * gq + 2], a[4 * gq + 3]);
+      }
+    }
+    lds_fence();
+    const auto rc = strip_rsrc(g.C[0], 32 * q, g.n, RB);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int u = i * WAVE + lane, r = u / 16, c = u % 16;
+      const float4 x = s4[r * 16 + (c ^ (r & 7))];
+      const uint2 y = rres[pr][i];
+      const float z0 = x.x + __uint_as_float(y.x << 16), z1 = x.y + __uint_as_float(y.x & 0xffff0000u);
+      const float z2 = x.z + __uint_as_float(y.y << 16), z3 = x.w + __uint_as_float(y.y & 0xffff0000u);
+      const uint2 v = make_uint2(bf16_rne(z0) | (bf16_rne(z1) << 16), bf16_rne(z2) | (bf16_rne(z3) << 16));
+      __builtin_amdgcn_raw_buffer_store_b64(
+          __builtin_bit_cast(decltype(__builtin_amdgcn_raw_buffer_load_b64(rc, 0, 0, 0)), v), rc,
+          r * RB + (half * DC + 64 * pr + 4 * c) * 2, 0, 0);
+    }
+    lds_fence();
+  };
+  v16f acc[NACC];
+#pragma unroll
+  for (int k = 0; k < NACC; ++k)
+#pragma unroll
+    for (int v = 0; v < 16; ++v) acc[k][v] = 0.f;
+  auto phase = [&](int64_t t, uint4 (&cur)[LPP]) {
+    const int64_t q = q0 + (t / P) * stride;
+    const int p = (int)(t % P);
+    put_phase(cur);
+    // the strip's residual, in its first phase and ahead of the prefetch, so
+    // that waiting for it (the memory counter is in order) leaves the
+    // prefetch in flight
+    if (p == 0) {
+#pragma unroll
+      for (int pr = 0; pr < J / 2; ++pr) load_resid(q, pr);
+    }
+    load_phase(cur, t + 2);
+    lds_fence();
+    uint4 bv[KS];
+#pragma unroll
+    for (int c = 0; c < KS; ++c) bv[c] = sl[m32 * CPR + ((2 * c + h) ^ (m32 & 7))];
+    lds_fence();
+    if constexpr (P == 1) {
+      v16f held;
+#pragma unroll
+      for (int j = 0; j < J; ++j) {
+        asm volatile("" ::: "memory");
+        v16f a;
+#pragma unroll
+        for (int v = 0; v < 16; ++v) a[v] = 0.f;
+        const T *wrow = Ws + (32 * j) * D;
+#pragma unroll
+        for (int c = 0; c < KS; ++c) {
+          if (c % 8 == 0 && c > 0) asm volatile("" ::: "memory");
+          const uint4 wv = *reinterpret_cast<const uint4 *>(wrow + woff[c % 4] + (c / 4) * 8 * AV);
+          a = M::mma(wv, bv[c], a);
+        }
+        if (j % 2 == 0) held = a;
+        else out_pair(q, j / 2, held, a);
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < J; ++j) {
+        asm volatile("" ::: "memory");
+        const T *wrow = Ws + (32 * j) * D;
+#pragma unroll
+        for (int c = 0; c < KS; ++c) {
+          const int kc = p * KS + c;
+          const uint4 wv = *reinterpret_cast<const uint4 *>(wrow + woff[kc % 4] + (kc / 4) * 8 * AV);
+          acc[j] = M::mma(wv, bv[c], acc[j]);
+        }
+      }
+      if (p == P - 1) {
+#pragma unroll
+        for (int j = 0; j < J; j += 2) {
+          out_pair(q, j / 2, acc[j], acc[j + 1]);
+#pragma unroll
+          for (int v = 0; v < 16; ++v) acc[j][v] = acc[j + 1][v] = 0.f;
+        }
+      }
+    }
+  };
+  uint4 g0[LPP], g1[LPP];
+  load_phase(g0, 0);
+  load_phase(g1, 1);
+  const int64_t nt = q0 < strips ? ((strips - 1 - q0) / stride + 1) * P : 0;
+  for (int64_t t = 0; t < nt; t += 2) {
+    phase(t, g0);
+    if (t + 1 >= nt) break;
+    phase(t + 1, g1);
+  }
+}
+
+// ---------------------------------------------------------------------------
 // four-source row GEMM (the input gradient): C = sum_s A_s W_s^T (all but
 // fp32 at D = 256).
 //
@@ -1084,6 +1284,17 @@ static void launch_resident_k(const RowsGemm &g, hipStream_t st) {
   k_rows_resident<T, D, RESID, NZ><<<grid, RR_THREADS, 0, st>>>(g, (int)groups);
 }
 
+template <int D, int NH>
+static void launch_staged_out(const RowsGemm &g, hipStream_t st) {
+  static const int per_cu = blocks_per_cu(k_rows_staged_out<D, NH>, RR_THREADS);
+  const int64_t strips = cdiv(g.n, 32);
+  const int64_t cus_per_xcd = std::max(1, device_cus() / 8);
+  int64_t groups = std::max<int64_t>(1, (int64_t)per_cu * cus_per_xcd / NH);
+  groups = std::max<int64_t>(1, std::min<int64_t>(groups, cdiv(strips, 8 * RR_WAVES)));
+  const dim3 grid((unsigned)(8 * groups * NH));
+  k_rows_staged_out<D, NH><<<grid, RR_THREADS, 0, st>>>(g, (int)groups);
+}
+
 template <int D, int NZ>
 static void launch_staged_k(const RowsGemm &g, hipStream_t st) {
   static const int per_cu = blocks_per_cu(k_rows_staged<D, NZ>, RR_THREADS);
@@ -1103,7 +1314,8 @@ template <typename T, int D>
 static void launch_resident(const RowsGemm &g, hipStream_t st) {
   constexpr bool three_fit = 3 * D * D * (int)sizeof(T) <= 128 * 1024;
   constexpr bool staged = sizeof(T) == 2 && (D == 128 || D == 256);
-  if (g.R) launch_resident_k<T, D, true, 1>(g, st);
+  if (g.R && staged) launch_staged_out<D, D == 256 ? 2 : 1>(g, st);
+  else if (g.R) launch_resident_k<T, D, true, 1>(g, st);
   else if (staged && g.nout == 3 && three_fit) launch_staged_k<D, three_fit ? 3 : 1>(g, st);
   else if (staged) launch_staged_k<D, 1>(g, st);
   else if (g.nout == 3 && three_fit) launch_resident_k<T, D, false, three_fit ? 3 : 1>(g, st);

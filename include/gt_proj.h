@@ -19,6 +19,8 @@
  * row-major in dtype dt (d = heads * head_dim, so [n, d] is the [n, heads,
  * head_dim] layout of gt_attn.h); weights W_* are [d, d] row-major in dt and
  * act as X W; weight gradients dW_* are [d, d] float32.  d in {64, 128, 256}.
+ * No output may overlap an input or another output (gt_proj_out, for one, has
+ * two workgroups share a node strip of X at d = 256, each writing half of Z).
  * The products run on the matrix cores with float32 accumulation; bf16
  * outputs are rounded to nearest even.  Results are bitwise deterministic:
  * the weight gradients sum per-slot partial products (slots of contiguous
