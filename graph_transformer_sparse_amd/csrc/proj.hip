@@ -1046,6 +1046,159 @@ __global__ __launch_bounds__(S4_THREADS) void k_rows_sum4(RowsGemm g) {
 }
 
 // ---------------------------------------------------------------------------
+// The input gradient for bf16 at D = 128 and 256: k_rows_sum4 with the
+// source strips and the results staged through LDS, as in k_rows_staged.
+// Each wavefront owns an 8 KB slice beside the weight slabs.  A source strip
+// comes in as contiguous 16-byte chunks (an instruction covers 4 rows x 256
+// bytes) in phases of 256 bytes of a row (one at D = 128, two at D = 256),
+// the next phase's loads in flight while this one is multiplied; the slice
+// hands the phase back in the operand layout.  The weight slabs stream
+// through LDS exactly as in k_rows_sum4 (double-buffered, one barrier a
+// slab), so the products and their order are the same.  Results leave
+// through the slice a pair of 32-column blocks at a time, 8 rows x 128
+// bytes per store.
+// ---------------------------------------------------------------------------
+template <int D>
+__global__ __launch_bounds__(S4_THREADS) void k_rows_sum4_staged(RowsGemm g) {
+  using T = bf16_t;
+  using M = Mma<T>;
+  constexpr int CH = D / 16, RB = 2 * D, JW = D / 32;
+  constexpr int PB = RB < 256 ? RB : 256;                 // bytes of a row per phase
+  constexpr int P = RB / PB;                              // phases per source
+  constexpr int CPP = PB / 32;                            // operand chunks per phase
+  constexpr int CPR = PB / 16;                            // 16-byte chunks of a row per phase
+  constexpr int LPP = 32 * CPR / WAVE;                    // loads per lane per phase
+  constexpr int NSLAB = CH / S4_NCS, SPP = CPP / S4_NCS;  // weight slabs per source, per phase
+  constexpr int SV = D * 2 * S4_NCS;
+  constexpr int SU = (SV + S4_THREADS - 1) / S4_THREADS;
+  static_assert(CPP % S4_NCS == 0 && NSLAB % 2 == 0 && P * CPP == CH && 32 * CPR * 16 >= 4096, "shape");
+  __shared__ __align__(16) char Bs[2][D * S4_PITCH];
+  __shared__ __align__(16) uint4 Sl[S4_WAVES][32 * CPR];
+  const int tid = threadIdx.x, lane = tid & (WAVE - 1), h = lane / 32, m32 = lane % 32;
+  const int w = __builtin_amdgcn_readfirstlane(tid / WAVE);
+  const int64_t nblk = (g.n + S4_ROWS - 1) / S4_ROWS;
+  const int64_t first = blockIdx.x, stride = gridDim.x;
+  uint4 *sl = Sl[w];
+
+  uint4 sv[SU];
+  int woff[SU];
+#pragma unroll
+  for (int i = 0; i < SU; ++i) {
+    const int u = (tid + i * S4_THREADS) % SV;
+    woff[i] = (u / (2 * S4_NCS)) * RB + (u % (2 * S4_NCS)) * 16;
+  }
+  auto fetch_w = [&](int s, int slab) {
+    const auto rw = __builtin_amdgcn_make_buffer_rsrc((void *)g.B[0][s], 0, D * RB, BUF_WORD3);
+#pragma unroll
+    for (int i = 0; i < SU; ++i)
+      sv[i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rw, woff[i], slab * S4_NCS * 32, 0));
+  };
+  auto put_w = [&](char *buf) {
+#pragma unroll
+    for (int i = 0; i < SU; ++i) {
+      const int u = tid + i * S4_THREADS;
+      if (u < SV) {
+        const int n = u / (2 * S4_NCS), v = u % (2 * S4_NCS);
+        *reinterpret_cast<uint4 *>(buf + n * S4_PITCH + v * 16) = sv[i];
+      }
+    }
+  };
+  auto strip_of = [&](int64_t blk) { return (blk * S4_WAVES + w) * 32; };   // first row
+  // phase ph of source s of the strip at row0 (rows past n read 0)
+  auto load_phase = [&](uint4 (&dst)[LPP], int s, int64_t row0, int ph) {
+    const auto ra = strip_rsrc(g.A[s], row0, g.n, RB);
+#pragma unroll
+    for (int i = 0; i < LPP; ++i) {
+      const int u = i * WAVE + lane, r = u / CPR, c = u % CPR;
+      dst[i] = __builtin_bit_cast(
+          uint4, __builtin_amdgcn_raw_buffer_load_b128(ra, r * RB + ph * PB + c * 16, 0, 0));
+    }
+  };
+  // the bf16 results of the block pair (j0, j0 + 1) for the strip at row0
+  auto out_pair = [&](int64_t row0, int j0, const v16f &a0, const v16f &a1) {
+    uint2 *s2 = reinterpret_cast<uint2 *>(sl);
+#pragma unroll
+    for (int bj = 0; bj < 2; ++bj) {
+      const v16f &a = bj ? a1 : a0;
+#pragma unroll
+      for (int gq = 0; gq < 4; ++gq) {
+        const int ch = 4 * bj + gq;
+        s2[2 * (m32 * 8 + (ch ^ (m32 & 7))) + h] =
+            make_uint2(bf16_rne(a[4 * gq]) | (bf16_rne(a[4 * gq + 1]) << 16),
+                       bf16_rne(a[4 * gq + 2]) | (bf16_rne(a[4 * gq + 3]) << 16));
+      }
+    }
+    lds_fence();
+    const auto rc = strip_rsrc(g.C[0], row0, g.n, RB);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int u = i * WAVE + lane, r = u / 8, c = u % 8;
+      const uint4 v = sl[r * 8 + (c ^ (r & 7))];
+      __builtin_amdgcn_raw_buffer_store_b128(
+          __builtin_bit_cast(decltype(__builtin_amdgcn_raw_buffer_load_b128(rc, 0, 0, 0)), v), rc,
+          r * RB + j0 * 64 + c * 16, 0, 0);
+    }
+    lds_fence();
+  };
+
+  uint4 gl[LPP];
+  load_phase(gl, 0, strip_of(first), 0);
+  fetch_w(0, 0);
+  put_w(Bs[0]);
+  for (int64_t blk = first; blk < nblk; blk += stride) {
+    const int64_t row0 = strip_of(blk);
+    v16f acc[JW];
+#pragma unroll
+    for (int j = 0; j < JW; ++j)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[j][v] = 0.f;
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+#pragma unroll
+      for (int ph = 0; ph < P; ++ph) {
+        // stage this phase, start the next one's loads, read it back (a
+        // second register set, two phases ahead, spills at D = 256 and
+        // made no measurable difference at D = 128)
+#pragma unroll
+        for (int i = 0; i < LPP; ++i) {
+          const int u = i * WAVE + lane, r = u / CPR, c = u % CPR;
+          sl[r * CPR + (c ^ (r & 7))] = gl[i];
+        }
+        if (ph + 1 < P) load_phase(gl, s, row0, ph + 1);
+        else if (s < 3) load_phase(gl, s + 1, row0, 0);
+        else load_phase(gl, 0, strip_of(blk + stride), 0);
+        lds_fence();
+        uint4 a[CPP];
+#pragma unroll
+        for (int c = 0; c < CPP; ++c) a[c] = sl[m32 * CPR + ((2 * c + h) ^ (m32 & 7))];
+        lds_fence();
+#pragma unroll
+        for (int sp = 0; sp < SPP; ++sp) {
+          const int slab = ph * SPP + sp;      // slab of this source
+          __syncthreads();                     // Bs[slab & 1] is complete
+          if (slab + 1 < NSLAB) fetch_w(s, slab + 1);
+          else fetch_w(s < 3 ? s + 1 : 0, 0);
+          const char *buf = Bs[slab & 1];
+#pragma unroll
+          for (int cc = 0; cc < S4_NCS; ++cc) {
+            asm volatile("" ::: "memory");     // one chunk's weight reads at a time
+#pragma unroll
+            for (int j = 0; j < JW; ++j) {
+              const uint4 wv = *reinterpret_cast<const uint4 *>(
+                  buf + (32 * j + m32) * S4_PITCH + (2 * cc + h) * 16);
+              acc[j] = M::mma(wv, a[sp * S4_NCS + cc], acc[j]);
+            }
+          }
+          put_w(Bs[(slab + 1) & 1]);
+        }
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < JW; j += 2) out_pair(row0, j, acc[j], acc[j + 1]);
+  }
+}
+
+// ---------------------------------------------------------------------------
 // weight gradient: dW_s = X^T G_s, a contraction over the n node rows.
 // The rows are cut into `slots` contiguous ranges; workgroup (s, slot)
 // computes the whole [D, D] product of its range for gradient s into
@@ -1314,21 +1467,30 @@ template <typename T, int D>
 static void launch_resident(const RowsGemm &g, hipStream_t st) {
   constexpr bool three_fit = 3 * D * D * (int)sizeof(T) <= 128 * 1024;
   constexpr bool staged = sizeof(T) == 2 && (D == 128 || D == 256);
-  if (g.R && staged) launch_staged_out<D, D == 256 ? 2 : 1>(g, st);
-  else if (g.R) launch_resident_k<T, D, true, 1>(g, st);
-  else if (staged && g.nout == 3 && three_fit) launch_staged_k<D, three_fit ? 3 : 1>(g, st);
-  else if (staged) launch_staged_k<D, 1>(g, st);
-  else if (g.nout == 3 && three_fit) launch_resident_k<T, D, false, three_fit ? 3 : 1>(g, st);
-  else launch_resident_k<T, D, false, 1>(g, st);
+  if constexpr (staged) {
+    if (g.R) launch_staged_out<D, D == 256 ? 2 : 1>(g, st);
+    else if (g.nout == 3 && three_fit) launch_staged_k<D, three_fit ? 3 : 1>(g, st);
+    else launch_staged_k<D, 1>(g, st);
+  } else {
+    if (g.R) launch_resident_k<T, D, true, 1>(g, st);
+    else if (g.nout == 3 && three_fit) launch_resident_k<T, D, false, three_fit ? 3 : 1>(g, st);
+    else launch_resident_k<T, D, false, 1>(g, st);
+  }
 }
 
 // transb = false: one source (NA = 1); transb = true: four (NA = 4)
 template <typename T, int D>
 static void launch_sum4(const RowsGemm &g, hipStream_t st) {
-  static const int per_cu = blocks_per_cu(k_rows_sum4<T, D>, S4_THREADS);
   const int64_t nblk = cdiv(g.n, S4_ROWS);
-  const int64_t grid = std::min<int64_t>(nblk, (int64_t)per_cu * device_cus());
-  k_rows_sum4<T, D><<<dim3((unsigned)grid), S4_THREADS, 0, st>>>(g);
+  if constexpr (sizeof(T) == 2 && (D == 128 || D == 256)) {
+    static const int per_cu = blocks_per_cu(k_rows_sum4_staged<D>, S4_THREADS);
+    const int64_t grid = std::min<int64_t>(nblk, (int64_t)per_cu * device_cus());
+    k_rows_sum4_staged<D><<<dim3((unsigned)grid), S4_THREADS, 0, st>>>(g);
+  } else {
+    static const int per_cu = blocks_per_cu(k_rows_sum4<T, D>, S4_THREADS);
+    const int64_t grid = std::min<int64_t>(nblk, (int64_t)per_cu * device_cus());
+    k_rows_sum4<T, D><<<dim3((unsigned)grid), S4_THREADS, 0, st>>>(g);
+  }
 }
 
 gt_status launch_rows_gemm(gt_dtype dt, RowsGemm g, int nout, bool transb, hipStream_t st) {
