@@ -1262,7 +1262,10 @@ void k_gemm_wgrad(WgradGemm g) {
   // staging registers of the next PD steps (a ring, indexed statically by
   // unrolling the step loop PD times); rows go through a buffer resource
   // bounded to the step's rows of the slot, so rows past the slot read as 0
-  constexpr int PD = (D == 256 && sizeof(T) == 4) ? 1 : (D == 256 ? 2 : 4);
+  // (bf16 at D = 256, 1M rows: 2 steps 0.79 ms, 3 steps 0.71, 4 steps 0.69,
+  // 5 steps 0.65, and 6 do not fit the registers; at D = 128, 2.4M rows, 6
+  // or 8 steps were slower than 4)
+  constexpr int PD = D == 256 ? (sizeof(T) == 4 ? 1 : 5) : 4;
   constexpr int RB = D * (int)sizeof(T);
   uint4 st[PD][2 * SU];
   // unit u: operand u / UOP, column group mg, row pair kp of the step
