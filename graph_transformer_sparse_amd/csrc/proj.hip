@@ -893,8 +893,9 @@ __global__ __launch_bounds__(RR_THREADS) void k_rows_staged_out(RowsGemm g, int 
 }
 
 // ---------------------------------------------------------------------------
-// four-source row GEMM (the input gradient): C = sum_s A_s W_s^T (all but
-// fp32 at D = 256).
+// four-source row GEMM (the input gradient): C = sum_s A_s W_s^T (fp32 at
+// D = 64 and 128, bf16 at D = 64; bf16 at D = 128 and 256 takes the staged
+// variant below, fp32 at D = 256 the column-tiled kernel).
 //
 // Each wavefront owns a 32-row strip and keeps the whole [32, D] result in
 // registers (J accumulator blocks) while the k dimension streams through in
@@ -1465,7 +1466,8 @@ static void launch_staged_k(const RowsGemm &g, hipStream_t st) {
 
 // all three Q/K/V weights stay in LDS together where they fit (128 KB), so
 // each strip of X is read once; otherwise workgroups split the outputs.
-// bf16 at D = 128 and 256 without a residual stages its strips through LDS.
+// bf16 at D = 128 and 256 stages its strips through LDS (the output
+// projection with its residual in k_rows_staged_out).
 template <typename T, int D>
 static void launch_resident(const RowsGemm &g, hipStream_t st) {
   constexpr bool three_fit = 3 * D * D * (int)sizeof(T) <= 128 * 1024;
