@@ -27,8 +27,8 @@ def _abs(x):
 
 
 CASES = [(n, d, dt) for dt in ("f32", "bf16") for n, d in
-         ((1, 64), (100, 128), (128, 256), (1000, 64), (4097, 128), (20000, 256),
-          (70001, 128), (50003, 256))]
+         ((1, 64), (1, 128), (1, 256), (33, 256), (100, 128), (128, 256), (257, 128),
+          (1000, 64), (4097, 128), (20000, 256), (70001, 128), (50003, 256))]
 
 
 @pytest.mark.parametrize("case", CASES, ids=[f"n{n}-d{d}-{dt}" for n, d, dt in CASES])
