@@ -561,17 +561,48 @@ __global__ void k_val_ptr(const int32_t *indptr, int64_t n_rows, int64_t nnz, Mi
   if (r < n_rows && indptr[r + 1] < indptr[r]) atomicOr(&m->csr_flags, 2u);
 }
 
-__global__ void k_val_edges(const int32_t *indptr, const int32_t *indices, int64_t n_rows,
-                            int64_t n_cols, int64_t nnz, Misc *m) {
-  const int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (e >= nnz) return;
-  const int32_t c = indices[e];
-  if (c < 0 || (int64_t)c >= n_cols) {
-    atomicMin(&m->csr_first, (uint32_t)(2 * e));
-    return;
+// Every edge: its column in range, and above the previous edge's column
+// unless it starts its row.  Runs once the row pointer has passed k_val_ptr
+// (so it is non-decreasing from 0 to nnz).  The first bad edge e is kept as
+// 2e (column out of range) or 2e + 1 (columns not increasing).  Rows are
+// found as in k_edge_rows: per tile of consecutive edges, in an LDS copy of
+// the row pointer between the tile's first and last row.
+__global__ __launch_bounds__(ER_THREADS) void k_val_edges(const int32_t *indptr,
+                                                          const int32_t *indices, int64_t n_rows,
+                                                          int64_t n_cols, int64_t nnz, Misc *m) {
+  __shared__ int32_t ip[ER_ROWS + 1];
+  __shared__ int32_t r01[2];
+  const int64_t e0 = (int64_t)blockIdx.x * ER_TILE;
+  const int64_t e1 = std::min<int64_t>(e0 + ER_TILE, nnz);   // exclusive
+  if (threadIdx.x < 2)
+    r01[threadIdx.x] = row_of_edge(indptr, n_rows, (int32_t)(threadIdx.x == 0 ? e0 : e1 - 1));
+  __syncthreads();
+  const int32_t r0 = r01[0];
+  const int64_t nr = (int64_t)r01[1] - r0 + 1;               // rows r0 .. r1
+  const bool local = nr <= ER_ROWS;
+  if (local)
+    for (int64_t k = threadIdx.x; k <= nr; k += ER_THREADS) ip[k] = indptr[r0 + k];
+  __syncthreads();
+  for (int64_t e = e0 + threadIdx.x; e < e1; e += ER_THREADS) {
+    const int32_t c = indices[e];
+    if (c < 0 || (int64_t)c >= n_cols) {
+      atomicMin(&m->csr_first, (uint32_t)(2 * e));
+      continue;
+    }
+    int32_t start;                       // the first edge of e's row
+    if (local) {
+      int lo = 0, hi = (int)nr;          // last k with ip[k] <= e, in [lo, hi)
+      while (hi - lo > 1) {
+        const int mid = (lo + hi) >> 1;
+        if (ip[mid] <= e) lo = mid;
+        else hi = mid;
+      }
+      start = ip[lo];
+    } else {
+      start = indptr[row_of_edge(indptr, n_rows, (int32_t)e)];
+    }
+    if (e > start && c <= indices[e - 1]) atomicMin(&m->csr_first, (uint32_t)(2 * e + 1));
   }
-  const int32_t r = row_of_edge(indptr, n_rows, (int32_t)e);
-  if (e > indptr[r] && c <= indices[e - 1]) atomicMin(&m->csr_first, (uint32_t)(2 * e + 1));
 }
 
 }  // namespace gt
@@ -703,8 +734,8 @@ extern "C" gt_status gt_csr_validate(const int32_t *indptr, const int32_t *indic
   } else if (h.csr_flags & 2u) {
     c = 2;
   } else if (nnz > 0) {
-    k_val_edges<<<dim3((unsigned)cdiv(nnz, TB)), dim3(TB), 0, s>>>(indptr, indices, n_rows, n_cols,
-                                                                    nnz, m);
+    k_val_edges<<<dim3((unsigned)cdiv(nnz, ER_TILE)), dim3(ER_THREADS), 0, s>>>(indptr, indices,
+                                                                               n_rows, n_cols, nnz, m);
     GT_CHECK_LAUNCH();
     GT_HIP(hipMemcpyAsync(&h, m, sizeof(Misc), hipMemcpyDeviceToHost, s));
     GT_HIP(hipStreamSynchronize(s));
