@@ -14,6 +14,17 @@ namespace gt {
 constexpr int32_t DEFAULT_T_SMALL = 32;
 constexpr int32_t DEFAULT_CHUNK = 256;
 
+// In the schedule over the rows of A, small rows are ordered by their degree
+// rounded down to a multiple of ROW_SMALL_CLASS (descending), then by id:
+// the four rows of a wavefront still have nearly equal lengths, and rows
+// with neighbouring ids, which share staged dbias lines (and, in graphs
+// whose ids carry locality, neighbours), run together.  Measured per step
+// against exact degrees: Hub 12.24 -> 12.13 ms, Mid 0.624 -> 0.619 ms,
+// Large 6.38 -> 6.36 ms, Shard unchanged.  The transpose's schedule keeps
+// exact degrees: there the same classes cost Shard, whose columns are 61 %
+// empty, 0.17 ms in the column pass.
+constexpr int32_t ROW_SMALL_CLASS = 4;
+
 // Pieces are dealt to the XCDs by their position in their segment, so the
 // shorter the pieces, the narrower the range of rows each XCD gathers at a
 // time (and the more merge work).  Measured with the dealt order, per step

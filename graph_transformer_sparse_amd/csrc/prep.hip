@@ -372,9 +372,15 @@ __global__ __launch_bounds__(DS_THREADS) void k_degree_stats(const int32_t *ptr,
   }
 }
 
-__global__ void k_degree_keys(const int32_t *ptr, int64_t n, uint32_t maxd, uint32_t *key) {
+// Sort keys of the degree order: maxd minus the degree, a small segment's
+// degree (at most t_small) rounded down to a multiple of cls; the stable sort
+// then breaks ties by id.
+__global__ void k_degree_keys(const int32_t *ptr, int64_t n, uint32_t maxd, int32_t t_small,
+                              int32_t cls, uint32_t *key) {
   const int64_t s = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (s < n) key[s] = maxd - (uint32_t)(ptr[s + 1] - ptr[s]);
+  if (s >= n) return;
+  const int32_t d = ptr[s + 1] - ptr[s];
+  key[s] = maxd - (uint32_t)(d <= t_small ? d - d % cls : d);
 }
 
 __global__ void k_piece_counts(const int32_t *ptr, const int32_t *order, int64_t nb,
@@ -432,6 +438,7 @@ struct SchedJob {
   int64_t n;            // segments
   Misc *misc_d;         // this schedule's device counters
   gt_sched *out;
+  int32_t small_class;  // small segments ordered by degree rounded down to a multiple of this
   Misc m;               // host copy of the counters
 };
 
@@ -503,7 +510,7 @@ static gt_status build_schedules(SchedJob (&jobs)[2], int32_t t_small, int32_t t
     const int64_t n = j.n;
     if (n > 0) {
       k_degree_keys<<<dim3((unsigned)cdiv(n, TB)), dim3(TB), 0, s>>>(j.ptr, n, j.m.max_degree,
-                                                                     b.kA);
+                                                                     t_small, j.small_class, b.kA);
       GT_CHECK_LAUNCH();
     }
     uint32_t *ks, *vs;
@@ -697,7 +704,8 @@ extern "C" gt_status gt_graph_prepare(const int32_t *indptr, const int32_t *indi
                                                                       g.indices_t);
     GT_CHECK_LAUNCH();
   }
-  SchedJob jobs[2] = {{indptr, n_rows, misc, &g.rows, {}}, {g.indptr_t, n_cols, misc + 1, &g.cols, {}}};
+  SchedJob jobs[2] = {{indptr, n_rows, misc, &g.rows, ROW_SMALL_CLASS, {}},
+                      {g.indptr_t, n_cols, misc + 1, &g.cols, 1, {}}};
   st = build_schedules(jobs, t_small, t_mid, chunk, b, s);
   if (st != GT_OK) return st;
   GT_HIP(hipStreamSynchronize(s));

@@ -85,7 +85,10 @@ typedef enum { GT_F32 = 0, GT_BF16 = 1 } gt_dtype;
 
 /* Degree-ordered work schedule of the segments (rows of the CSR, or rows
  * of its transpose = columns of A).  Definition:
- *   order    = segment ids sorted by degree descending, ties by ascending id;
+ *   order    = segment ids sorted by degree descending, ties by ascending id,
+ *              except that in the schedule over the rows of A (`rows`) a
+ *              small segment (degree <= t_small) counts its degree rounded
+ *              down to a multiple of 4, so each such class runs in id order;
  *   n_big    = #segments with degree >  t_mid   (they lead `order`);
  *   n_mid    = #segments with t_small < degree <= t_mid (next in `order`);
  *   n_small  = #segments with degree <= t_small (the tail of `order`);

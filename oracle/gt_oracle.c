@@ -91,7 +91,10 @@ void or_transpose(i64 R, i64 M, i64 E, const i32 *indptr, const i32 *indices,
 }
 
 /* The degree-ordered work schedule, from its definition:
- *   order  = segment ids sorted by (degree descending, id ascending);
+ *   order  = segment ids sorted by (order degree descending, id ascending),
+ *            the order degree being the degree, or for a small segment
+ *            (degree <= t_small) the degree rounded down to a multiple of
+ *            small_class (so small segments stay at the tail);
  *   n_big  = #segments with degree >  t_mid;
  *   n_mid  = #segments with t_small < degree <= t_mid;
  *   n_small= #segments with degree <= t_small;
@@ -146,20 +149,31 @@ static void deal_by_position(i64 ni, i32 *items) {
   free(pieces);
 }
 
+/* The degree a segment is ordered by: its degree, except that a small one
+ * (degree <= t_small) counts its degree rounded down to a multiple of
+ * small_class. */
 static const i32 *g_sort_ptr;
+static i32 g_sort_small, g_sort_class;
+static i32 order_degree(i32 s) {
+  i32 d = g_sort_ptr[s + 1] - g_sort_ptr[s];
+  return d <= g_sort_small ? d - d % g_sort_class : d;
+}
 static int cmp_deg_desc(const void *a, const void *b) {
   i32 x = *(const i32 *)a, y = *(const i32 *)b;
-  i32 dx = g_sort_ptr[x + 1] - g_sort_ptr[x], dy = g_sort_ptr[y + 1] - g_sort_ptr[y];
+  i32 dx = order_degree(x), dy = order_degree(y);
   if (dx != dy) return dx > dy ? -1 : 1;
   return (x > y) - (x < y);
 }
 
-i64 or_schedule(i64 n, const i32 *ptr, i32 t_small, i32 t_mid, i32 chunk, i32 *order,
+i64 or_schedule(i64 n, const i32 *ptr, i32 t_small, i32 t_mid, i32 chunk, i32 small_class,
+                i32 *order,
                 i32 *counts /* [3] big, mid, small */, i32 *items /* [cap][4] */,
                 i64 cap_items, i32 *merges /* [cap][3] */, i64 cap_merges,
                 i64 *n_merges_out) {
   for (i64 s = 0; s < n; ++s) order[s] = (i32)s;
   g_sort_ptr = ptr;
+  g_sort_small = t_small;
+  g_sort_class = small_class > 0 ? small_class : 1;
   qsort(order, (size_t)n, sizeof(i32), cmp_deg_desc);
   i32 nb = 0, nm = 0, ns = 0;
   for (i64 s = 0; s < n; ++s) {

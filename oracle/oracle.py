@@ -49,7 +49,7 @@ def lib():
         L.or_transpose.restype = None
         L.or_transpose.argtypes = [_i64, _i64, _i64, _P, _P, _P, _P, _P]
         L.or_schedule.restype = _i64
-        L.or_schedule.argtypes = [_i64, _P, _i32, _i32, _i32, _P, _P, _P, _i64, _P, _i64, _P]
+        L.or_schedule.argtypes = [_i64, _P, _i32, _i32, _i32, _i32, _P, _P, _P, _i64, _P, _i64, _P]
         L.or_set_threads.argtypes = [_int]
         L.or_get_threads.restype = _int
         att = [_i64, _i64, _int, _int, _dbl, _P, _P, _P, _P, _P, _P]
@@ -102,9 +102,12 @@ def transpose(indptr, indices, n_cols: int):
     return pt, it, pm
 
 
-def schedule(ptr, t_small: int, t_mid: int, chunk: int):
+def schedule(ptr, t_small: int, t_mid: int, chunk: int, small_class: int = 1):
     """Degree-ordered schedule of the segments of ``ptr`` (rows of a CSR or
-    columns of its transpose).  Returns dict(order, counts, items, merges)."""
+    columns of its transpose).  Segments go by descending degree, ties by id,
+    a small segment's degree (at most t_small) rounded down to a multiple of
+    ``small_class`` (4 in the library's schedule over the rows of A, 1 over
+    its transpose).  Returns dict(order, counts, items, merges)."""
     ptr = _i32a(ptr)
     n = ptr.size - 1
     E = int(ptr[-1])
@@ -114,7 +117,7 @@ def schedule(ptr, t_small: int, t_mid: int, chunk: int):
     items = np.empty((cap, 4), np.int32)
     merges = np.empty((cap, 3), np.int32)
     nm = np.zeros(1, np.int64)
-    ni = lib().or_schedule(n, _p(ptr), t_small, t_mid, chunk, _p(order), _p(counts),
+    ni = lib().or_schedule(n, _p(ptr), t_small, t_mid, chunk, small_class, _p(order), _p(counts),
                            _p(items), cap, _p(merges), cap, _p(nm))
     assert ni >= 0
     return dict(order=order, counts=counts, items=items[:ni].copy(),

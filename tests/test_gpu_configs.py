@@ -206,7 +206,7 @@ def test_prep_full_configs(name):
     assert (ts, tm, ch) == T.gt_graph_thresholds(ix.size)
     print(f"prep {name}: oracle schedules", flush=True)
     for which, ptr in (("rows", ip), ("cols", pt)):
-        got, want = g.schedule(which), O.schedule(ptr, ts, tm, ch)
+        got, want = g.schedule(which), O.schedule(ptr, ts, tm, ch, 4 if which == "rows" else 1)
         assert np.array_equal(got["order"].cpu().numpy(), want["order"]), which
         assert tuple(got["counts"]) == tuple(int(c) for c in want["counts"]), which
         assert np.array_equal(got["items"].cpu().numpy(), want["items"]), which

@@ -46,8 +46,11 @@ GRAPHS = _graphs()
 THRESH = [(32, 2048, 2048), (2, 8, 8), (0, 0, 1), (4, 16, 5), (3, 3, 1000)]
 
 
-def _check_sched(got, ptr, ts, tm, ch):
-    want = O.schedule(ptr, ts, tm, ch)
+ROW_CLASS = 4   # small rows of A are ordered by degree rounded down to a multiple of 4
+
+
+def _check_sched(got, ptr, ts, tm, ch, cls=1):
+    want = O.schedule(ptr, ts, tm, ch, cls)
     np.testing.assert_array_equal(got["order"].cpu().numpy(), want["order"])
     assert tuple(got["counts"]) == tuple(int(c) for c in want["counts"])
     np.testing.assert_array_equal(got["items"].cpu().numpy(), want["items"])
@@ -70,7 +73,7 @@ def test_transpose_and_schedules(gi, th):
     np.testing.assert_array_equal(g.indptr_t.cpu().numpy(), pt)
     np.testing.assert_array_equal(g.indices_t.cpu().numpy(), it)
     np.testing.assert_array_equal(g.perm.cpu().numpy(), pm)
-    _check_sched(g.schedule("rows"), ip, *th)
+    _check_sched(g.schedule("rows"), ip, *th, ROW_CLASS)
     _check_sched(g.schedule("cols"), pt, *th)
 
 
@@ -85,7 +88,7 @@ def test_mid_config_prep():
     np.testing.assert_array_equal(g.perm.cpu().numpy(), pm)
     ts, tm, ch = g.st.t_small, g.st.t_mid, g.st.chunk   # what prepare chose for this size
     assert (ts, tm, ch) == T.gt_graph_thresholds(ix.size)
-    _check_sched(g.schedule("rows"), ip, ts, tm, ch)
+    _check_sched(g.schedule("rows"), ip, ts, tm, ch, ROW_CLASS)
     _check_sched(g.schedule("cols"), pt, ts, tm, ch)
 
 
@@ -139,6 +142,6 @@ def test_tier_env_overrides(monkeypatch):
     monkeypatch.setenv("GT_TIER_CHUNK", "2")
     g = T.gt_graph_prepare(dev(ip), dev(ix), 4)
     assert (g.st.t_small, g.st.t_mid, g.st.chunk) == (1, 2, 2)
-    _check_sched(g.schedule("rows"), ip, 1, 2, 2)
+    _check_sched(g.schedule("rows"), ip, 1, 2, 2, ROW_CLASS)
     g = T.gt_graph_prepare(dev(ip), dev(ix), 4, 0, 8, 8)
     assert (g.st.t_small, g.st.t_mid, g.st.chunk) == (0, 8, 8)

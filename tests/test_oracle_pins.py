@@ -461,14 +461,19 @@ def test_csr_check():
     assert O.csr_check(np.array([0, 2, 3, 4], np.int32), ix, 3) == 1
 
 
+@pytest.mark.parametrize("cls", [1, 4])
 @pytest.mark.parametrize("ts,tm,ch", [(2, 8, 16), (32, 256, 4096), (0, 0, 1), (4, 4, 5)])
-def test_schedule_definition(ts, tm, ch):
+def test_schedule_definition(ts, tm, ch, cls):
     degs = np.concatenate([np.random.default_rng(1).integers(0, 60, 300), [200, 64, 65, 63, 0, 17]])
     ptr = np.zeros(degs.size + 1, np.int32)
     np.cumsum(degs, out=ptr[1:])
-    S = O.schedule(ptr, ts, tm, ch)
-    # order: numpy's stable sort by descending degree
-    np.testing.assert_array_equal(S["order"], np.argsort(-degs, kind="stable"))
+    S = O.schedule(ptr, ts, tm, ch, cls)
+    # order: numpy's stable sort by descending degree, small degrees (at most
+    # ts) first rounded down to a multiple of cls
+    deg_order = np.where(degs <= ts, degs - degs % cls, degs)
+    np.testing.assert_array_equal(S["order"], np.argsort(-deg_order, kind="stable"))
+    if cls > 1 and ts >= cls:
+        assert not np.array_equal(S["order"], np.argsort(-degs, kind="stable"))
     nb, nm, ns = S["counts"]
     assert nb == (degs > tm).sum() and nm == ((degs > ts) & (degs <= tm)).sum() and ns == (degs <= ts).sum()
     dealt = S["items"]
