@@ -461,10 +461,11 @@ def test_csr_check():
     assert O.csr_check(np.array([0, 2, 3, 4], np.int32), ix, 3) == 1
 
 
+@pytest.mark.parametrize("seed", [1, 2, 3])
 @pytest.mark.parametrize("cls", [1, 4])
 @pytest.mark.parametrize("ts,tm,ch", [(2, 8, 16), (32, 256, 4096), (0, 0, 1), (4, 4, 5)])
-def test_schedule_definition(ts, tm, ch, cls):
-    degs = np.concatenate([np.random.default_rng(1).integers(0, 60, 300), [200, 64, 65, 63, 0, 17]])
+def test_schedule_definition(ts, tm, ch, cls, seed):
+    degs = np.concatenate([np.random.default_rng(seed).integers(0, 60, 300), [200, 64, 65, 63, 0, 17]])
     ptr = np.zeros(degs.size + 1, np.int32)
     np.cumsum(degs, out=ptr[1:])
     S = O.schedule(ptr, ts, tm, ch, cls)
