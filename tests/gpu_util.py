@@ -37,9 +37,12 @@ def to_np(t):
 U32 = 2.0 ** -24
 
 
-def assert_close(got, ref, rtol, name, mag=None, head_axis="auto"):
+def assert_close(got, ref, rtol, name, mag=None, head_axis="auto", extra=None):
     """head_axis: the axis whose entries get their own statistics (default:
-    axis 1 of a [n, heads, head_dim] array; None: the whole array)."""
+    axis 1 of a [n, heads, head_dim] array; None: the whole array).  extra
+    (optional, like ref): a further elementwise error bound that the inputs
+    themselves set (see the wide-score-range test), added to the elementwise
+    bound and, as its L2 norm, to the relative L2 one."""
     g = got if isinstance(got, np.ndarray) else to_np(got)
     ref = np.asarray(ref, np.float64)
     assert g.shape == ref.shape, (name, g.shape, ref.shape)
@@ -51,11 +54,14 @@ def assert_close(got, ref, rtol, name, mag=None, head_axis="auto"):
     rms = np.sqrt(np.mean(ref ** 2, axis=axes, keepdims=True))
     d2 = np.sqrt(np.sum((g - ref) ** 2, axis=axes))
     r2 = np.sqrt(np.sum(ref ** 2, axis=axes))
-    ok = (d2 <= rtol * r2) | (r2 == 0)       # an all-zero reference is left to the elementwise bound
-    assert np.all(ok), f"{name}: relative L2 error {d2 / np.maximum(r2, 1e-300)} > {rtol}"
+    x2 = 0.0 if extra is None else np.sqrt(np.sum(np.asarray(extra, np.float64) ** 2, axis=axes))
+    ok = (d2 <= rtol * r2 + x2) | (r2 == 0)  # an all-zero reference is left to the elementwise bound
+    assert np.all(ok), f"{name}: relative L2 error {d2 / np.maximum(r2, 1e-300)} > {rtol} (+ {x2})"
     bound = rtol * np.abs(ref) + rtol * rms
     if mag is not None:
         bound = bound + 8 * U32 * np.asarray(mag, np.float64)
+    if extra is not None:
+        bound = bound + np.asarray(extra, np.float64)
     err = np.abs(g - ref)
     bad = ~(err <= bound)
     if bad.any():

@@ -6,6 +6,9 @@
   columns with ragged last pieces), rectangular adjacencies, every supported
   head count / head size / dtype, with and without bias;
 * the 2,000-node config in full, under several thresholds;
+* -inf-masked edges, and scores spread over hundreds (running maxima that
+  move in most rounds, weights that underflow), against bounds derived from
+  the float32 rounding of the scores;
 * bitwise determinism.
 The large configurations are in test_gpu_configs.py.
 """
@@ -17,7 +20,7 @@ from graph_transformer_sparse_amd import gtattn as T
 from graph_transformer_sparse_amd import inputs as I
 from oracle import oracle as O
 
-from gpu_util import RTOL, assert_close, assert_lse, device_problem
+from gpu_util import RTOL, U32, assert_close, assert_lse, device_problem
 
 pytestmark = pytest.mark.gpu
 
@@ -137,6 +140,82 @@ def test_minus_inf_bias_masks_edges(dt, H, dh):
         for t in out:
             assert not torch.isnan(t).any()
         check_full(P, out)
+
+
+def _wide_problem(dt, H, dh):
+    """A graph with rows of up to 600 edges and a bias ramp of 1 per edge,
+    rising along even rows and falling along odd ones."""
+    import dataclasses
+    rng = np.random.default_rng(91)
+    R, M = 150, 700
+    degs = np.array([1, 2, 3, 9, 65, 130, 257, 600] + list(rng.integers(0, 300, R - 8)))
+    rng.shuffle(degs)
+    ip, ix = I.random_graph(91, R, M, degs, self_loops=False)
+    P = I.small_problem(91, ip, ix, M, H, dh, dt, True)
+    src = np.repeat(np.arange(R), np.diff(ip))
+    ramp = (np.arange(ip[-1]) - ip[src]) * np.where(src % 2 == 0, 1.0, -1.0)
+    return dataclasses.replace(P, bias=(P.bias + ramp[:, None]).astype(np.float32))
+
+
+def score_rounding_bounds(P, lse, U, Ymag):
+    """First-order bounds on what float32 rounding of the scores does to each
+    output, with eps_i = u max_e [(dh + 3) S_e + 3 |b_e| + |lse_i|] over the
+    edges e of row i, S_e = scale sum_c |q_c k_c|:
+      weight U_e:  2 eps_i U_e (its own change and the normalisation's);
+      D_i:         2 eps_i A_i,  A_i = sum_e U_e |dU_e| <= <|dY_i|, Ymag_i>;
+      dS_e:        2 eps_i U_e (|dY_i|.|V_j| + 2 A_i)  (also dbias);
+      Y_i:         2 eps_i Ymag_i;
+      dQ, dK, dV:  the dS_e and weight bounds times |K_j|, |Q_i|, |dY_i|,
+                   summed over the row or column.
+    bf16 configs stage (p, w) per edge in bf16 for dbias: 2^-9 U_e
+    (|dU_e| + 3 A_i) more.  Every bound is returned doubled."""
+    ip, ix = P.indptr, P.indices
+    R, M = ip.size - 1, P.K.shape[0]
+    H, dh, sc = P.Q.shape[1], P.Q.shape[2], P.scale
+    src = np.repeat(np.arange(R), np.diff(ip))
+    S = sc * np.einsum("ehc,ehc->eh", np.abs(P.Q[src]), np.abs(P.K[ix]))
+    lmag = np.where(np.isfinite(lse), np.abs(lse), 0.0)
+    eps = np.zeros((R, H))
+    np.maximum.at(eps, src, U32 * ((dh + 3) * S + 3 * np.abs(P.bias) + lmag[src]))
+    A = np.einsum("rhc,rhc->rh", np.abs(P.dY), Ymag)
+    dUabs = np.einsum("ehc,ehc->eh", np.abs(P.dY[src]), np.abs(P.V[ix]))
+    dW = 2 * eps[src] * U
+    dS = dW * (dUabs + 2 * A[src])
+    b = {"Y": 2 * eps[:, :, None] * Ymag, "dbias": dS.copy(),
+         "dQ": np.zeros((R, H, dh)), "dK": np.zeros((M, H, dh)), "dV": np.zeros((M, H, dh))}
+    np.add.at(b["dQ"], src, sc * dS[:, :, None] * np.abs(P.K[ix]))
+    np.add.at(b["dK"], ix, sc * dS[:, :, None] * np.abs(P.Q[src]))
+    np.add.at(b["dV"], ix, dW[:, :, None] * np.abs(P.dY[src]))
+    if P.cfg.dtype == "bf16":
+        b["dbias"] += 2.0 ** -9 * U * (dUabs + 3 * A[src])
+    return {k: 2 * v for k, v in b.items()}
+
+
+@pytest.mark.parametrize("dt, H, dh", [("f32", 4, 16), ("bf16", 4, 32), ("f32", 1, 64)])
+def test_wide_score_range(dt, H, dh):
+    """Scores spread over hundreds: along the rows of a bias ramp the running
+    maximum moves up in most rounds (rescaling the state each time) or stays
+    at the first edge, more than half of the weights underflow to 0 in
+    float32, and the pieces of split rows merge with shifts far apart.  The
+    float32 rounding of the scores themselves then bounds the accuracy
+    (score_rounding_bounds), which is added to the usual tolerance."""
+    P = _wide_problem(dt, H, dh)
+    ip, ix, M, sc = P.indptr, P.indices, P.cfg.n_cols, P.scale
+    m = {}
+    rY, rl, rU = O.fwd(ip, ix, M, P.Q, P.K, P.V, P.bias, sc, want_U=True, mag=m)
+    rQ, rK, rV, rB = O.bwd(ip, ix, M, P.Q, P.K, P.V, P.dY, P.bias, sc, mag=m)
+    assert np.ptp(P.bias) > 800 and np.mean(rU < 1e-38) > 0.5
+    extra = score_rounding_bounds(P, rl, rU, m["Y"])
+    rtol = RTOL[dt]
+    for th in (None, (2, 8, 8), (0, 0, 3)):
+        print(f"wide scores {dt} H={H} dh={dh} th={th}", flush=True)
+        Y, lse, dQ, dK, dV, dB = run_gpu(P, th)
+        assert_lse(lse, rl, 1e-5 if dt == "f32" else 1e-4)
+        assert_close(Y, rY, rtol, "Y", m["Y"], extra=extra["Y"])
+        assert_close(dQ, rQ, rtol, "dQ", m["dQ"], extra=extra["dQ"])
+        assert_close(dK, rK, rtol, "dK", m["dK"], extra=extra["dK"])
+        assert_close(dV, rV, rtol, "dV", m["dV"], extra=extra["dV"])
+        assert_close(dB, rB, rtol, "dbias", head_axis=1, extra=extra["dbias"])
 
 
 def test_bitwise_determinism():
