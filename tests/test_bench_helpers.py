@@ -71,3 +71,16 @@ def test_counter_records_are_gated_by_the_source_hash(tmp_path, monkeypatch):
     (tmp_path / "profiles" / "traffic_fwd_x.txt").write_text(
         f"source_hash: {bench.kernel_source_hash()}\nhbm_bytes_per_launch: 123\n")
     assert bench.traffic_record("fwd", "x") == 123.0
+
+
+def test_more_than_one_gpu_is_refused():
+    """bench.py measures one GPU: --gpus above 1 exits with status 2 and a
+    message, before anything touches a device."""
+    import os
+    import subprocess
+    import sys
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    r = subprocess.run([sys.executable, os.path.join(root, "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True, timeout=120, cwd=root)
+    assert r.returncode == 2
+    assert "one GPU only" in r.stderr and r.stdout == ""
