@@ -1,5 +1,5 @@
 """The benchmark's host-side helpers, on the CPU: the byte models against
-the per-pass figures the survey of the pages tabulates, the compulsory-byte
+per-pass figures worked out by hand for the Hub workload, the compulsory-byte
 count, the parity verdict of a timed run (it must pass the oracle's own
 outputs and fail a perturbed one), and the stored counter records (used
 only on the sources they were taken on)."""
