@@ -9,6 +9,7 @@
 * -inf-masked edges, and scores spread over hundreds (running maxima that
   move in most rounds, weights that underflow), against bounds derived from
   the float32 rounding of the scores;
+* bf16 outputs rounded to nearest even wherever the float32 result decides it;
 * bitwise determinism.
 The large configurations are in test_gpu_configs.py.
 """
@@ -20,7 +21,7 @@ from graph_transformer_sparse_amd import gtattn as T
 from graph_transformer_sparse_amd import inputs as I
 from oracle import oracle as O
 
-from gpu_util import RTOL, U32, assert_close, assert_lse, device_problem
+from gpu_util import RTOL, U32, assert_close, assert_lse, device_problem, to_np
 
 pytestmark = pytest.mark.gpu
 
@@ -216,6 +217,46 @@ def test_wide_score_range(dt, H, dh):
         assert_close(dK, rK, rtol, "dK", m["dK"], extra=extra["dK"])
         assert_close(dV, rV, rtol, "dV", m["dV"], extra=extra["dV"])
         assert_close(dB, rB, rtol, "dbias", head_axis=1, extra=extra["dbias"])
+
+
+def _bf16_round(x, ties_even=True):
+    """fp64 -> the nearest bfloat16 value (8 significant bits), ties to even;
+    with ties_even=False, toward zero (truncation), for the test's own check."""
+    x = np.asarray(x, np.float64)
+    m, e = np.frexp(x)
+    q = np.round(m * 256.0) if ties_even else np.trunc(m * 256.0)
+    return np.ldexp(q, e - 8)
+
+
+@pytest.mark.parametrize("bias", [False, True], ids=["nobias", "bias"])
+def test_bf16_outputs_round_to_nearest_even(bias):
+    """bf16 outputs are the float32 results rounded to nearest, ties to even.
+    Where the oracle's value lies farther from a rounding midpoint than the
+    float32 parity bound (1e-5 |r| + 1e-5 rms + 8 u mag, which the float32
+    tests hold the same arithmetic to), the rounded value is decided, and
+    the GPU's must equal the oracle's rounded to nearest even.  Truncation
+    would differ on a large share of those elements (checked here on the
+    oracle's own values)."""
+    rng = np.random.default_rng(123)
+    R = M = 300
+    ip, ix = I.random_graph(123, R, M, rng.integers(1, 60, R))
+    P = I.small_problem(123, ip, ix, M, 4, 32, "bf16", bias)
+    m = {}
+    rY, _ = O.fwd(ip, ix, M, P.Q, P.K, P.V, P.bias, P.scale, mag=m)
+    rQ, rK, rV, _ = O.bwd(ip, ix, M, P.Q, P.K, P.V, P.dY, P.bias, P.scale, mag=m)
+    Y, _, dQ, dK, dV, _ = run_gpu(P)
+    for name, got, r in (("Y", Y, rY), ("dQ", dQ, rQ), ("dK", dK, rK), ("dV", dV, rV)):
+        g = to_np(got)
+        near = _bf16_round(r)
+        ulp = np.ldexp(1.0, np.frexp(r)[1] - 8)
+        rms = np.sqrt(np.mean(r ** 2, axis=(0, 2), keepdims=True))
+        margin = 1e-5 * np.abs(r) + 1e-5 * rms + 8 * U32 * m[name]
+        decided = (r != 0) & (ulp / 2 - np.abs(r - near) > margin)
+        assert decided.mean() > 0.9, (name, decided.mean())
+        assert np.mean(_bf16_round(r, ties_even=False)[decided] != near[decided]) > 0.3
+        bad = decided & (g != near)
+        assert not bad.any(), (f"{name}: {int(bad.sum())} of {int(decided.sum())} decided elements "
+                               f"differ from round-to-nearest-even")
 
 
 def test_bitwise_determinism():
