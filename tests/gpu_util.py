@@ -72,6 +72,40 @@ def assert_close(got, ref, rtol, name, mag=None, head_axis="auto", extra=None):
                              f"rel l2 {rel:.3e}")
 
 
+def bf16_round(x, ties_even=True):
+    """fp64 -> the nearest bfloat16 value (8 significant bits), ties to even;
+    with ties_even=False, toward zero (truncation: the tests' own check that
+    the comparison below tells the two apart)."""
+    x = np.asarray(x, np.float64)
+    m, e = np.frexp(x)
+    q = np.round(m * 256.0) if ties_even else np.trunc(m * 256.0)
+    return np.ldexp(q, e - 8)
+
+
+def assert_rounded_to_nearest_even(got, ref, mag, name, head_axis="auto"):
+    """bf16 outputs are the float32 results rounded to nearest, ties to even.
+    Where the oracle's value lies farther from a rounding midpoint than the
+    float32 parity bound (1e-5 |r| + 1e-5 rms + 8 u mag), the rounded value is
+    decided, and the GPU's must equal the oracle's rounded to nearest even.
+    Also checks that such elements are most of the tensor and that truncation
+    would differ on a large share of them."""
+    g = got if isinstance(got, np.ndarray) else to_np(got)
+    ref = np.asarray(ref, np.float64)
+    if head_axis == "auto":
+        head_axis = 1 if ref.ndim == 3 else None
+    axes = tuple(a for a in range(ref.ndim) if a != head_axis)
+    rms = np.sqrt(np.mean(ref ** 2, axis=axes, keepdims=True))
+    near = bf16_round(ref)
+    ulp = np.ldexp(1.0, np.frexp(ref)[1] - 8)
+    margin = 1e-5 * np.abs(ref) + 1e-5 * rms + 8 * U32 * np.asarray(mag, np.float64)
+    decided = (ref != 0) & (ulp / 2 - np.abs(ref - near) > margin)
+    assert decided.mean() > 0.9, (name, decided.mean())
+    assert np.mean(bf16_round(ref, ties_even=False)[decided] != near[decided]) > 0.3, name
+    bad = decided & (g != near)
+    assert not bad.any(), (f"{name}: {int(bad.sum())} of {int(decided.sum())} decided elements "
+                           f"differ from round-to-nearest-even")
+
+
 def assert_lse(got, ref, rtol, name="lse"):
     g = got if isinstance(got, np.ndarray) else to_np(got)
     ref = np.asarray(ref, np.float64)

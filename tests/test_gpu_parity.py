@@ -21,7 +21,8 @@ from graph_transformer_sparse_amd import gtattn as T
 from graph_transformer_sparse_amd import inputs as I
 from oracle import oracle as O
 
-from gpu_util import RTOL, U32, assert_close, assert_lse, device_problem, to_np
+from gpu_util import (RTOL, U32, assert_close, assert_lse, assert_rounded_to_nearest_even,
+                      device_problem)
 
 pytestmark = pytest.mark.gpu
 
@@ -219,24 +220,10 @@ def test_wide_score_range(dt, H, dh):
         assert_close(dB, rB, rtol, "dbias", head_axis=1, extra=extra["dbias"])
 
 
-def _bf16_round(x, ties_even=True):
-    """fp64 -> the nearest bfloat16 value (8 significant bits), ties to even;
-    with ties_even=False, toward zero (truncation), for the test's own check."""
-    x = np.asarray(x, np.float64)
-    m, e = np.frexp(x)
-    q = np.round(m * 256.0) if ties_even else np.trunc(m * 256.0)
-    return np.ldexp(q, e - 8)
-
-
 @pytest.mark.parametrize("bias", [False, True], ids=["nobias", "bias"])
 def test_bf16_outputs_round_to_nearest_even(bias):
-    """bf16 outputs are the float32 results rounded to nearest, ties to even.
-    Where the oracle's value lies farther from a rounding midpoint than the
-    float32 parity bound (1e-5 |r| + 1e-5 rms + 8 u mag, which the float32
-    tests hold the same arithmetic to), the rounded value is decided, and
-    the GPU's must equal the oracle's rounded to nearest even.  Truncation
-    would differ on a large share of those elements (checked here on the
-    oracle's own values)."""
+    """bf16 outputs are the float32 results rounded to nearest, ties to even,
+    wherever the float32 result decides it (assert_rounded_to_nearest_even)."""
     rng = np.random.default_rng(123)
     R = M = 300
     ip, ix = I.random_graph(123, R, M, rng.integers(1, 60, R))
@@ -246,17 +233,7 @@ def test_bf16_outputs_round_to_nearest_even(bias):
     rQ, rK, rV, _ = O.bwd(ip, ix, M, P.Q, P.K, P.V, P.dY, P.bias, P.scale, mag=m)
     Y, _, dQ, dK, dV, _ = run_gpu(P)
     for name, got, r in (("Y", Y, rY), ("dQ", dQ, rQ), ("dK", dK, rK), ("dV", dV, rV)):
-        g = to_np(got)
-        near = _bf16_round(r)
-        ulp = np.ldexp(1.0, np.frexp(r)[1] - 8)
-        rms = np.sqrt(np.mean(r ** 2, axis=(0, 2), keepdims=True))
-        margin = 1e-5 * np.abs(r) + 1e-5 * rms + 8 * U32 * m[name]
-        decided = (r != 0) & (ulp / 2 - np.abs(r - near) > margin)
-        assert decided.mean() > 0.9, (name, decided.mean())
-        assert np.mean(_bf16_round(r, ties_even=False)[decided] != near[decided]) > 0.3
-        bad = decided & (g != near)
-        assert not bad.any(), (f"{name}: {int(bad.sum())} of {int(decided.sum())} decided elements "
-                               f"differ from round-to-nearest-even")
+        assert_rounded_to_nearest_even(got, r, m[name], name)
 
 
 def test_bitwise_determinism():

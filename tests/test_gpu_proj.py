@@ -6,7 +6,9 @@ Tolerance as for attention (gpu_util): per tensor relative L2 <= rtol and
 elementwise rtol*|r| + rtol*rms(r) + 8u*mag, mag = the sum of the absolute
 values of each output's terms (|A| |B| for a product A B).  Weight
 gradients are float32 for either input dtype and sum exact products of the
-inputs, so they are held to the float32 bound (1e-5) in both cases.
+inputs, so they are held to the float32 bound (1e-5) in both cases.  bf16
+outputs are also pinned to round-to-nearest-even where the float32 result
+decides the rounding.
 """
 import numpy as np
 import pytest
@@ -17,7 +19,7 @@ from graph_transformer_sparse_amd import inputs as I
 from oracle import layer as L
 from oracle import oracle as O
 
-from gpu_util import RTOL, TDT, assert_close, dev, to_np
+from gpu_util import RTOL, TDT, assert_close, assert_rounded_to_nearest_even, dev, to_np
 
 pytestmark = pytest.mark.gpu
 
@@ -56,6 +58,28 @@ def test_projection_kernels(case):
     for got, ref, a, k in zip(dW, rdw, (dZ, *G), "oqkv"):
         assert_close(got, ref, 1e-5, "dW" + k, _abs(X).T @ _abs(a))
     torch.cuda.synchronize()
+
+
+@pytest.mark.parametrize("n, d", [(1000, 64), (4097, 128), (20000, 256)])
+def test_bf16_projections_round_to_nearest_even(n, d):
+    """The bf16 results of Q/K/V, Z (its residual added in float32 before the
+    one rounding) and dX are the float32 results rounded to nearest, ties to
+    even, wherever the float32 result decides it (at d = 64 the resident
+    kernels, at 128 and 256 the staged ones)."""
+    X, W, dZ = I.layer_inputs(710 + d, n, d, "bf16")
+    G = [I.layer_inputs(810 + k, n, d, "bf16")[2] for k in range(3)]
+    Y = I.layer_inputs(910, n, d, "bf16")[2]
+    t = lambda a: dev(a, torch.bfloat16)
+    Xd, Wd = t(X), {k: t(v) for k, v in W.items()}
+    Q, K, V = T.gt_proj_qkv(Xd, Wd["q"], Wd["k"], Wd["v"])
+    for got, ref, k in zip((Q, K, V), L.proj_qkv(X, W["q"], W["k"], W["v"]), "qkv"):
+        assert_rounded_to_nearest_even(got, ref, _abs(X) @ _abs(W[k]), "XW" + k)
+    Z = T.gt_proj_out(Xd, Wd["o"], t(Y))
+    assert_rounded_to_nearest_even(Z, L.proj_out(X, W["o"], Y), _abs(X) @ _abs(W["o"]) + _abs(Y), "Z")
+    dX = T.gt_proj_bwd_data(t(dZ), t(G[0]), t(G[1]), t(G[2]), Wd["o"], Wd["q"], Wd["k"], Wd["v"])
+    mag = sum(_abs(a) @ _abs(W[k]).T for a, k in zip((dZ, *G), "oqkv"))
+    assert_rounded_to_nearest_even(dX, L.proj_bwd_data(dZ, G[0], G[1], G[2], W["o"], W["q"], W["k"], W["v"]),
+                                   mag, "dX")
 
 
 def test_weight_gradient_is_deterministic():
