@@ -6,6 +6,8 @@ module imports nothing from it.
 
 The wrapper only builds the shared library, marshals numpy arrays and
 allocates outputs; every step of the computation is in gt_oracle.c.
+GT_ORACLE_LIB, when set, names another build of gt_oracle.c to load instead
+(the tests' check that the pins fail on planted mistakes).
 """
 from __future__ import annotations
 
@@ -42,7 +44,7 @@ _P = C.c_void_p
 def lib():
     global _lib
     if _lib is None:
-        path = build(force=False)
+        path = os.environ.get("GT_ORACLE_LIB") or build(force=False)
         L = C.CDLL(path)
         L.or_csr_check.restype = _int
         L.or_csr_check.argtypes = [_i64, _i64, _i64, _P, _P]

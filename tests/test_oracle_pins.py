@@ -457,6 +457,8 @@ def test_csr_check():
     assert O.csr_check(ip, ix, 3) == 0
     assert O.csr_check(ip, np.array([0, 3, 1], np.int32), 3) == 3
     assert O.csr_check(ip, np.array([2, 0, 1], np.int32), 3) == 4
+    assert O.csr_check(ip, np.array([2, 2, 1], np.int32), 3) == 4     # a duplicate column
+    assert O.csr_check(ip, np.array([-1, 2, 1], np.int32), 3) == 3
     assert O.csr_check(np.array([0, 2, 1, 3], np.int32), ix, 3) == 2
     assert O.csr_check(np.array([0, 2, 3, 4], np.int32), ix, 3) == 1
 
